@@ -1,0 +1,17 @@
+"""fp64 CPU oracle for the paged KV-cache decode path.
+
+TEST INFRASTRUCTURE: only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no
+code with the HIP library or its Python binding.
+"""
+from .pagedkv_oracle import (  # noqa: F401
+    brute_ref,
+    contiguous_ref,
+    copy_ref,
+    decode_ref,
+    gather_sequence,
+    softmax_attention,
+    splitk_ref,
+    widen,
+    write_ref,
+)

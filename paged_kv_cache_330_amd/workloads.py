@@ -1,0 +1,360 @@
+"""Seeded synthetic workloads for the paged decode path.
+
+This module only draws inputs: sequence lengths, the physical block pool and
+its free order, block tables and slot numbers (through ``BlockManager``), and
+the Q/K/V values.  It holds none of the attention, write or copy arithmetic,
+and it is the one piece of code that both the GPU path's callers and the
+oracle's callers use, so that both see identical inputs.
+
+Five decode workloads are defined, each named by what it is:
+
+1. ``tiny_mha``: fp32, 4 sequences of lengths {5, 17, 32, 40}, 2 q heads = 2 kv
+   heads, head_dim 64, block_size 16, a pool of 16 blocks handed out in a
+   seeded random order, scale 1/sqrt(64).
+2. ``llama7b_mha``: bf16, 64 sequences, lengths uniform on [128, 2048],
+   32 q = 32 kv heads, head_dim 128, block_size 16.
+3. ``llama3_8b_gqa``: bf16, 256 sequences, lengths lognormal (median 1024,
+   sigma 1 in log space) clipped to [16, 8192], 32 q / 8 kv heads, head_dim 128,
+   block_size 16.
+4. ``long_context``: bf16, 8 sequences of 32768 tokens, 64 q / 8 kv heads,
+   head_dim 128, block_size 32 or 64; 1% of K rows are multiplied by 8 to
+   stretch the softmax range.
+5. ``prefix_sharing``: bf16, 4 prompts x 8 samples, 32 q / 8 kv heads,
+   head_dim 128, block_size 8 or 16; each prompt's prefix blocks are shared by
+   its 8 samples, which then grow 256-token tails (``PrefixSharingWorkload``).
+
+Recipe (numpy ``default_rng(seed)``, draws in this order): lengths; the free
+order of the pool (a permutation); q; K; V; the outlier mask.  Values are
+binary32 normal draws rounded to bfloat16 with round-to-nearest-even for the
+bf16 workloads.  Pool size is ceil(1.1 * blocks needed) unless fixed.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+from .block_manager import BlockManager
+
+__all__ = [
+    "CONFIGS",
+    "bf16_round",
+    "DecodeWorkload",
+    "make_decode_workload",
+    "PrefixSharingWorkload",
+]
+
+
+def bf16_round(x) -> np.ndarray:
+    """binary32 -> bfloat16 bit patterns (uint16), round to nearest even.
+
+    Input generation only.  The inputs never hold NaN or infinity.
+    """
+    bits = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((bits >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((bits + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+@dataclass(frozen=True)
+class ConfigSpec:
+    name: str
+    dtype: str
+    num_seqs: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    seed: int
+    lengths: str            # "fixed", "uniform", "lognormal"
+    fixed_lens: Sequence[int] = ()
+    num_blocks: Optional[int] = None
+    k_outlier_frac: float = 0.0
+    k_outlier_mult: float = 8.0
+
+
+CONFIGS: Dict[int, ConfigSpec] = {
+    1: ConfigSpec("tiny_mha", "f32", 4, 2, 2, 64, 16, 1, "fixed", (5, 17, 32, 40), num_blocks=16),
+    2: ConfigSpec("llama7b_mha", "bf16", 64, 32, 32, 128, 16, 2, "uniform"),
+    3: ConfigSpec("llama3_8b_gqa", "bf16", 256, 32, 8, 128, 16, 3, "lognormal"),
+    4: ConfigSpec("long_context", "bf16", 8, 64, 8, 128, 32, 4, "fixed", (32768,) * 8,
+                  k_outlier_frac=0.01),
+    5: ConfigSpec("prefix_sharing", "bf16", 32, 32, 8, 128, 16, 5, "prefix"),
+}
+
+
+def _normal(rng, shape, dtype: str) -> np.ndarray:
+    x = rng.standard_normal(shape, dtype=np.float32)
+    return x if dtype == "f32" else bf16_round(x)
+
+
+def _draw_lengths(spec: ConfigSpec, rng, num_seqs: int) -> np.ndarray:
+    if spec.lengths == "fixed":
+        lens = np.array(list(spec.fixed_lens)[:num_seqs], dtype=np.int64)
+        if len(lens) < num_seqs:
+            lens = np.resize(lens, num_seqs)
+        return lens
+    if spec.lengths == "uniform":
+        return rng.integers(128, 2048, size=num_seqs, endpoint=True).astype(np.int64)
+    if spec.lengths == "lognormal":
+        z = rng.standard_normal(num_seqs)
+        return np.clip(np.rint(1024.0 * np.exp(z)), 16, 8192).astype(np.int64)
+    raise ValueError(spec.lengths)
+
+
+@dataclass
+class DecodeWorkload:
+    """One decode step: prefill state, the step's writes, then attention.
+
+    ``k_tokens``/``v_tokens`` hold every sequence's tokens in logical order,
+    concatenated (``cu_seqlens`` delimits them); the last token of each
+    sequence is the one this step writes.  ``prefill_rows``/``prefill_slots``
+    put all earlier tokens into the pool, ``step_rows``/``step_slots`` the new
+    ones.
+    """
+    name: str
+    dtype: str
+    seed: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    scale: np.float32
+    seq_lens: np.ndarray
+    cu_seqlens: np.ndarray
+    q: np.ndarray
+    k_tokens: np.ndarray
+    v_tokens: np.ndarray
+    block_tables: np.ndarray
+    prefill_rows: np.ndarray
+    prefill_slots: np.ndarray
+    step_rows: np.ndarray
+    step_slots: np.ndarray
+    copy_pairs: np.ndarray
+    fresh_blocks_in_step: int = 0
+    manager: Optional[BlockManager] = field(default=None, repr=False)
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.seq_lens.shape[0])
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_tables.shape[1])
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    def seq_tokens(self, b: int):
+        """Logical ``[L_b, Hkv, D]`` K and V of sequence ``b`` (views)."""
+        s, e = int(self.cu_seqlens[b]), int(self.cu_seqlens[b + 1])
+        return self.k_tokens[s:e], self.v_tokens[s:e]
+
+    def empty_caches(self, fill: str = "nan"):
+        """Host K and V pools; unused slots hold NaN (``"nan"``) or zero."""
+        shape = (self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim)
+        if self.dtype == "f32":
+            val = np.float32(np.nan) if fill == "nan" else np.float32(0)
+            return np.full(shape, val, np.float32), np.full(shape, val, np.float32)
+        val = 0x7FC0 if fill == "nan" else 0
+        return np.full(shape, val, np.uint16), np.full(shape, val, np.uint16)
+
+    def kv_bytes(self) -> int:
+        """K+V bytes the decode step must read: sum_b L_b * Hkv * D * 2 * elem."""
+        return int(self.seq_lens.sum()) * self.num_kv_heads * self.head_dim * 2 * self.elem_bytes
+
+
+def make_decode_workload(config: int, *, block_size: Optional[int] = None,
+                         num_seqs: Optional[int] = None,
+                         seq_lens: Optional[Sequence[int]] = None,
+                         seed: Optional[int] = None,
+                         table_pad: int = 0) -> DecodeWorkload:
+    """Build decode workload ``config`` (1-4), optionally resized.
+
+    ``seq_lens`` replaces the length draw (the draw is still made so that the
+    later draws do not move); ``num_seqs`` changes the batch.
+    """
+    spec = CONFIGS[config]
+    if spec.lengths == "prefix":
+        raise ValueError("use PrefixSharingWorkload for the prefix-sharing workload")
+    bs = spec.block_size if block_size is None else int(block_size)
+    seed = spec.seed if seed is None else int(seed)
+    B = spec.num_seqs if num_seqs is None else int(num_seqs)
+    if seq_lens is not None:
+        B = len(seq_lens)
+    rng = np.random.default_rng(seed)
+    lens = _draw_lengths(spec, rng, B)
+    if seq_lens is not None:
+        lens = np.asarray(seq_lens, dtype=np.int64)
+    if (lens < 1).any():
+        raise ValueError("every sequence holds at least its new token")
+    need = int(sum(math.ceil(int(L) / bs) for L in lens))
+    NB = spec.num_blocks if (spec.num_blocks is not None and block_size is None
+                             and seq_lens is None and num_seqs is None) else math.ceil(1.1 * need)
+    NB = max(NB, need)
+    order = rng.permutation(NB)
+    mgr = BlockManager(NB, bs, order)
+    Hq, Hkv, D = spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    cu = np.zeros(B + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(lens)
+    T = int(cu[-1])
+
+    prefill_rows, prefill_slots = [], []
+    for b in range(B):
+        mgr.add_sequence(b)
+        slots, cows = mgr.append_tokens(b, int(lens[b]) - 1)
+        assert not cows
+        prefill_rows.append(np.arange(cu[b], cu[b + 1] - 1))
+        prefill_slots.append(np.asarray(slots, dtype=np.int64))
+    step_slots, fresh = [], 0
+    for b in range(B):
+        fresh += int((int(lens[b]) - 1) % bs == 0)
+        s, cow = mgr.append_token(b)
+        assert cow is None
+        step_slots.append(s)
+
+    q = _normal(rng, (B, Hq, D), spec.dtype)
+    k = _normal(rng, (T, Hkv, D), spec.dtype)
+    v = _normal(rng, (T, Hkv, D), spec.dtype)
+    if spec.k_outlier_frac > 0:
+        mask = rng.random((T, Hkv)) < spec.k_outlier_frac
+        if spec.dtype == "bf16":
+            kf = (k[mask].astype(np.uint32) << np.uint32(16)).view(np.float32)
+            k[mask] = bf16_round(kf * np.float32(spec.k_outlier_mult))
+        else:
+            k[mask] = k[mask] * np.float32(spec.k_outlier_mult)
+
+    width = max(math.ceil(int(L) / bs) for L in lens)
+    return DecodeWorkload(
+        name=spec.name, dtype=spec.dtype, seed=seed, num_q_heads=Hq, num_kv_heads=Hkv,
+        head_dim=D, block_size=bs, num_blocks=NB,
+        scale=np.float32(1.0 / math.sqrt(D)),
+        seq_lens=lens.astype(np.int32), cu_seqlens=cu, q=q, k_tokens=k, v_tokens=v,
+        block_tables=mgr.tables_array(list(range(B)), width=width, pad=table_pad),
+        prefill_rows=np.concatenate(prefill_rows) if prefill_rows else np.zeros(0, np.int64),
+        prefill_slots=np.concatenate(prefill_slots) if prefill_slots else np.zeros(0, np.int64),
+        step_rows=(cu[1:] - 1).astype(np.int64), step_slots=np.asarray(step_slots, np.int64),
+        copy_pairs=np.zeros((0, 2), np.int64), fresh_blocks_in_step=fresh, manager=mgr)
+
+
+@dataclass
+class SharingStep:
+    """Inputs of one decode step of the prefix-sharing workload."""
+    step: int
+    q: np.ndarray               # [B, Hq, D]
+    k_new: np.ndarray           # [B, Hkv, D]: the token each sample writes
+    v_new: np.ndarray
+    slot_mapping: np.ndarray    # [B] int64
+    copy_pairs: np.ndarray      # [n, 2] int64, to run before the writes
+    block_tables: np.ndarray    # [B, MB] int32
+    seq_lens: np.ndarray        # [B] int32
+
+
+class PrefixSharingWorkload:
+    """Parallel sampling over shared prompt prefixes.
+
+    ``prompts`` prompts of ``prefix_len`` tokens are prefilled once each; every
+    prompt is forked into ``samples`` sequences that reference the prompt's
+    blocks (reference count = samples).  Step ``s`` (1-based) has every sample
+    write its token at position ``prefix_len + s - 1`` and then attend over
+    ``prefix_len + s`` tokens.  When the last prefix block is only partly full,
+    the first step copies it for every sharer but the last, which writes in
+    place ("PagedAttention 动态内存分页", "写时复制与内存共享").
+    """
+
+    def __init__(self, prefix_len: int = 2044, tail_len: int = 256, block_size: int = 16,
+                 prompts: int = 4, samples: int = 8, seed: int = 5,
+                 num_q_heads: int = 32, num_kv_heads: int = 8, head_dim: int = 128):
+        self.prefix_len, self.tail_len, self.block_size = prefix_len, tail_len, block_size
+        self.prompts, self.samples, self.seed = prompts, samples, seed
+        self.num_q_heads, self.num_kv_heads, self.head_dim = num_q_heads, num_kv_heads, head_dim
+        self.dtype = "bf16"
+        self.scale = np.float32(1.0 / math.sqrt(head_dim))
+        self.num_seqs = prompts * samples
+        # Size the pool by a dry run of the whole schedule, then add 10%.
+        dry = BlockManager(10 ** 7, block_size)
+        self._schedule(dry, run_steps=tail_len)
+        self.blocks_needed = dry.peak_used
+        self.num_blocks = math.ceil(1.1 * self.blocks_needed)
+        rng = np.random.default_rng(seed)
+        self._order = rng.permutation(self.num_blocks)
+        Hkv, D = num_kv_heads, head_dim
+        self.prefix_k = bf16_round(rng.standard_normal((prompts, prefix_len, Hkv, D), dtype=np.float32))
+        self.prefix_v = bf16_round(rng.standard_normal((prompts, prefix_len, Hkv, D), dtype=np.float32))
+        self.tail_k = bf16_round(rng.standard_normal((self.num_seqs, tail_len, Hkv, D), dtype=np.float32))
+        self.tail_v = bf16_round(rng.standard_normal((self.num_seqs, tail_len, Hkv, D), dtype=np.float32))
+        self.width = math.ceil((prefix_len + tail_len) / block_size)
+        self.reset()
+
+    def _schedule(self, mgr: BlockManager, run_steps: int):
+        for p in range(self.prompts):
+            mgr.add_sequence((p, 0))
+            mgr.append_tokens((p, 0), self.prefix_len)
+            for j in range(1, self.samples):
+                mgr.fork((p, 0), (p, j))
+        for _ in range(run_steps):
+            for p in range(self.prompts):
+                for j in range(self.samples):
+                    mgr.append_token((p, j))
+
+    def reset(self) -> None:
+        """Start over from an empty pool (same seeded free order)."""
+        self.manager = BlockManager(self.num_blocks, self.block_size, self._order)
+        self.steps_done = 0
+        self._prefilled = False
+
+    @property
+    def seq_ids(self) -> List:
+        return [(p, j) for p in range(self.prompts) for j in range(self.samples)]
+
+    def prefill(self):
+        """Prefill every prompt once; returns ``(k [4P,Hkv,D], v, slots [4P])``."""
+        assert not self._prefilled
+        slots = []
+        for p in range(self.prompts):
+            self.manager.add_sequence((p, 0))
+            s, cows = self.manager.append_tokens((p, 0), self.prefix_len)
+            assert not cows
+            slots.extend(s)
+            for j in range(1, self.samples):
+                self.manager.fork((p, 0), (p, j))
+        self._prefilled = True
+        Hkv, D = self.num_kv_heads, self.head_dim
+        return (self.prefix_k.reshape(-1, Hkv, D), self.prefix_v.reshape(-1, Hkv, D),
+                np.asarray(slots, dtype=np.int64))
+
+    def next_step(self) -> SharingStep:
+        assert self._prefilled and self.steps_done < self.tail_len
+        s = self.steps_done + 1
+        slots, pairs = [], []
+        for sid in self.seq_ids:
+            slot, cow = self.manager.append_token(sid)
+            slots.append(slot)
+            if cow is not None:
+                pairs.append(cow)
+        self.steps_done = s
+        rng = np.random.default_rng((self.seed, s))
+        q = bf16_round(rng.standard_normal((self.num_seqs, self.num_q_heads, self.head_dim),
+                                           dtype=np.float32))
+        return SharingStep(
+            step=s, q=q, k_new=self.tail_k[:, s - 1].copy(), v_new=self.tail_v[:, s - 1].copy(),
+            slot_mapping=np.asarray(slots, dtype=np.int64),
+            copy_pairs=np.asarray(pairs, dtype=np.int64).reshape(-1, 2),
+            block_tables=self.manager.tables_array(self.seq_ids, width=self.width),
+            seq_lens=np.full(self.num_seqs, self.prefix_len + s, dtype=np.int32))
+
+    def logical_tokens(self, b: int, length: int):
+        """Sample ``b``'s first ``length`` tokens in logical order (K, V)."""
+        p = b // self.samples
+        n_tail = length - self.prefix_len
+        k = np.concatenate([self.prefix_k[p], self.tail_k[b, :n_tail]])
+        v = np.concatenate([self.prefix_v[p], self.tail_v[b, :n_tail]])
+        return k, v
+
+    def empty_caches(self, fill: str = "nan"):
+        shape = (self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim)
+        val = 0x7FC0 if fill == "nan" else 0
+        return np.full(shape, val, np.uint16), np.full(shape, val, np.uint16)
