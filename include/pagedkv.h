@@ -1,0 +1,151 @@
+/*
+ * pagedkv.h - C ABI of the MI355X (gfx950) paged KV-cache decode path.
+ *
+ * The KV cache of one attention layer is a pool of equal physical blocks,
+ * one pool for K and one for V, each laid out as
+ *     [num_blocks][block_size][num_kv_heads][head_dim]
+ * ("Paged KV" wiki, section "初始化阶段": the KV memory is cut into N equal
+ * physical blocks of shape [block_size, num_kv_heads, head_dim]; the
+ * K/V pair and the per-layer factor of that formula are kept as separate
+ * per-layer pools here).  A sequence reaches its tokens through a block
+ * table: entry j is the physical block that holds its logical block j
+ * ("Paged KV", section "运行阶段").  A slot number names one token row of the
+ * pool: slot = physical_block * block_size + offset_in_block.
+ *
+ * Conventions common to every call:
+ *   - Every pointer argument is a DEVICE pointer owned by the caller; the
+ *     library allocates no memory and keeps no pointer after the call returns.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
+ *     default stream) and returns as soon as its kernels are queued.
+ *   - Host-checkable mistakes return a negative pkv_status before anything is
+ *     launched; pkv_last_error() then describes the mistake.  Launch failures
+ *     return PKV_ERR_HIP.
+ *   - Device data (slots, block ids, sequence lengths, copy pairs) are checked
+ *     in the kernels: an out-of-range value is skipped (never dereferenced) and
+ *     recorded in a per-device error word that pkv_check_device_errors() reads.
+ *   - Base pointers of caches, K/V rows, q, out and workspace must be 16-byte
+ *     aligned; int32/int64 arrays must be naturally aligned.
+ *   - Supported: dtype PKV_F32 or PKV_BF16; head_dim 64 or 128; block_size
+ *     8, 16, 32 or 64; num_q_heads / num_kv_heads in {1, 2, 4, 8}.
+ */
+#ifndef PAGEDKV_H_
+#define PAGEDKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = -1, /* null/misaligned pointer, negative size, bad shape */
+  PKV_ERR_UNSUPPORTED = -2, /* dtype, head_dim, block_size or group not built */
+  PKV_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  PKV_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+} pkv_status;
+
+/* Shape and element type of one K (and the matching V) block pool. */
+typedef struct {
+  int64_t num_blocks;   /* physical blocks in each pool */
+  int32_t block_size;   /* tokens per block */
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;        /* pkv_dtype of the stored elements */
+} pkv_cache_desc;
+
+/*
+ * Slot-mapping scatter ("Paged KV", "运行阶段": each new token's K/V go into the
+ * next slot of the sequence's active block; prefill fills blocks in order).
+ *
+ *   k, v          [num_tokens][num_kv_heads][head_dim], cache->dtype, read.
+ *   slot_mapping  [num_tokens] int64; token i is copied bitwise to row
+ *                 slot_mapping[i] of both pools; -1 skips the token.  Slots
+ *                 must be distinct within one call (else which token lands is
+ *                 unspecified); a slot >= num_blocks*block_size is skipped and
+ *                 flagged in the device error word.
+ *   k_cache, v_cache  the pools, written only at the named slots.
+ * num_tokens == 0 is a no-op.
+ */
+int pkv_kv_write(const void* k, const void* v, const int64_t* slot_mapping,
+                 int64_t num_tokens, void* k_cache, void* v_cache,
+                 const pkv_cache_desc* cache, void* stream);
+
+/*
+ * Whole-block copies for copy-on-write of shared blocks ("PagedAttention
+ * 动态内存分页", section "写时复制与内存共享": sharers reference the same
+ * physical block until one must write, which copies it first).
+ *
+ *   src_dst_pairs  [num_pairs][2] int64 (src, dst).  For every pair the whole
+ *                  K block and the whole V block (all block_size slots) of
+ *                  src are copied to dst.  The dsts must be distinct and no
+ *                  dst may be a src in the same call, so that every read sees
+ *                  the pre-call pool.  Out-of-range ids are skipped and
+ *                  flagged in the device error word.
+ * num_pairs == 0 is a no-op.
+ */
+int pkv_block_copy(void* k_cache, void* v_cache, const pkv_cache_desc* cache,
+                   const int64_t* src_dst_pairs, int64_t num_pairs, void* stream);
+
+/*
+ * Bytes of device workspace pkv_attention_decode needs for these sizes: the
+ * per-partition partial results (running max, running sum and unnormalised
+ * output, fp32) of the split-K decomposition.  0 when every sequence fits in
+ * one partition.  partition_tokens 0 selects the default (512).
+ */
+size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                     int32_t max_blocks_per_seq, int32_t block_size,
+                                     int32_t partition_tokens);
+
+/*
+ * Decode-step attention over the paged pools ("Paged KV", section
+ * "Attention Kernel 的适配": the kernel takes the block table and block_size
+ * in addition, and reads K/V block by block through the table).  For query
+ * head h of sequence b, with G = num_q_heads / num_kv_heads and
+ * kv = h / G (consecutive grouping):
+ *     out[b][h] = sum_t softmax_t(scale * <q[b][h], K_t>) * V_t
+ * over the t < seq_lens[b] tokens reached through block_tables[b].
+ * The sum runs over partitions of partition_tokens tokens whose partial
+ * results are merged by max/sum rescaling.
+ *
+ *   out           [num_seqs][num_q_heads][head_dim], out_dtype (PKV_F32 or
+ *                 PKV_BF16, round to nearest even), written.  A sequence of
+ *                 length 0 gets a zero row.
+ *   q             [num_seqs][num_q_heads][head_dim], cache->dtype, read.
+ *   block_tables  [num_seqs][max_blocks_per_seq] int32, read; only the first
+ *                 ceil(seq_lens[b] / block_size) entries of a row are read.
+ *   seq_lens      [num_seqs] int32, tokens cached for each sequence (the
+ *                 newest included); must be <= max_blocks_per_seq*block_size.
+ *   scale         softmax scale applied to the fp32 dot products.
+ *   partition_tokens  0 (default 512) or a multiple of 64 and of block_size.
+ *   workspace     pkv_attention_workspace_bytes(...) bytes (may be NULL when
+ *                 that is 0), overwritten.
+ * Pools, q, tables and lengths are only read.  num_seqs == 0 is a no-op.
+ */
+int pkv_attention_decode(void* out, int32_t out_dtype, const void* q,
+                         const void* k_cache, const void* v_cache,
+                         const pkv_cache_desc* cache,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                         float scale, int32_t partition_tokens,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Message for the last non-OK return on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/*
+ * Synchronises `stream`, then reads and clears the current device's error
+ * word.  Returns PKV_OK if no kernel recorded a bad slot, block id, sequence
+ * length or copy pair since the last check; otherwise PKV_ERR_INVALID_ARG
+ * with the offending kinds in pkv_last_error().
+ */
+int pkv_check_device_errors(void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H_ */

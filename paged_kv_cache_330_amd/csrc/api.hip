@@ -1,0 +1,270 @@
+// C ABI of libpagedkv: argument validation, kernel choice and launch.
+// Declarations and contracts: include/pagedkv.h.
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+
+#include "pagedkv.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+WorkspaceLayout workspace_layout(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim,
+                                 int64_t max_parts) {
+  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * max_parts;
+  WorkspaceLayout l;
+  l.max_off = 0;
+  l.sum_off = up(rows * sizeof(float));
+  l.acc_off = l.sum_off + up(rows * sizeof(float));
+  l.total = l.acc_off + up(rows * head_dim * sizeof(float));
+  return l;
+}
+
+}  // namespace pkv
+
+namespace {
+
+// One error word per device; kernels OR range-check failures into it.
+__device__ unsigned g_device_error;
+
+constexpr int kMaxDevices = 64;
+unsigned* g_error_word[kMaxDevices];
+std::mutex g_error_mutex;
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Address of the current device's error word (looked up once per device).
+int error_word(unsigned** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(PKV_ERR_HIP, "device ordinal %d too large", dev);
+  std::lock_guard<std::mutex> lock(g_error_mutex);
+  if (!g_error_word[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_device_error));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(error word)");
+    g_error_word[dev] = static_cast<unsigned*>(p);
+  }
+  *out = g_error_word[dev];
+  return PKV_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int elem_bytes(int32_t dtype) { return dtype == PKV_F32 ? 4 : 2; }
+
+int check_cache(const pkv_cache_desc* c) {
+  if (!c) return fail(PKV_ERR_INVALID_ARG, "cache descriptor is NULL");
+  if (c->num_blocks < 0 || c->num_blocks > (int64_t(1) << 40))
+    return fail(PKV_ERR_INVALID_ARG, "num_blocks %lld out of range", (long long)c->num_blocks);
+  if (c->dtype != PKV_F32 && c->dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "cache dtype %d is neither PKV_F32 nor PKV_BF16", c->dtype);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d is not 64 or 128", c->head_dim);
+  if (c->block_size != 8 && c->block_size != 16 && c->block_size != 32 && c->block_size != 64)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size %d is not 8, 16, 32 or 64", c->block_size);
+  if (c->num_kv_heads < 1 || c->num_kv_heads > 1024)
+    return fail(PKV_ERR_INVALID_ARG, "num_kv_heads %d out of range", c->num_kv_heads);
+  return PKV_OK;
+}
+
+int check_ptr(const void* p, size_t align, const char* name) {
+  if (!p) return fail(PKV_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned(p, align)) return fail(PKV_ERR_INVALID_ARG, "%s is not %zu-byte aligned", name, align);
+  return PKV_OK;
+}
+
+#define PKV_TRY(x)             \
+  do {                         \
+    int _s = (x);              \
+    if (_s != PKV_OK) return _s; \
+  } while (0)
+
+int resolve_partition(int32_t partition_tokens, int32_t block_size, int32_t* part) {
+  const int32_t p = partition_tokens == 0 ? pkv::kDefaultPartitionTokens : partition_tokens;
+  if (p < 64 || p % 64 != 0 || p % block_size != 0)
+    return fail(PKV_ERR_INVALID_ARG,
+                "partition_tokens %d must be 0 or a positive multiple of 64 and of block_size %d",
+                partition_tokens, block_size);
+  *part = p;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+int pkv_kv_write(const void* k, const void* v, const int64_t* slot_mapping, int64_t num_tokens,
+                 void* k_cache, void* v_cache, const pkv_cache_desc* cache, void* stream) {
+  g_last_error.clear();
+  PKV_TRY(check_cache(cache));
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "num_tokens %lld < 0", (long long)num_tokens);
+  if (num_tokens == 0) return PKV_OK;
+  PKV_TRY(check_ptr(k, 16, "k"));
+  PKV_TRY(check_ptr(v, 16, "v"));
+  PKV_TRY(check_ptr(slot_mapping, 8, "slot_mapping"));
+  PKV_TRY(check_ptr(k_cache, 16, "k_cache"));
+  PKV_TRY(check_ptr(v_cache, 16, "v_cache"));
+  unsigned* err = nullptr;
+  PKV_TRY(error_word(&err));
+  const int64_t row_bytes =
+      static_cast<int64_t>(cache->num_kv_heads) * cache->head_dim * elem_bytes(cache->dtype);
+  hipError_t e = pkv::launch_kv_write(k, v, slot_mapping, num_tokens, k_cache, v_cache,
+                                      cache->num_blocks * cache->block_size, row_bytes, err,
+                                      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "kv_write launch");
+}
+
+int pkv_block_copy(void* k_cache, void* v_cache, const pkv_cache_desc* cache,
+                   const int64_t* src_dst_pairs, int64_t num_pairs, void* stream) {
+  g_last_error.clear();
+  PKV_TRY(check_cache(cache));
+  if (num_pairs < 0) return fail(PKV_ERR_INVALID_ARG, "num_pairs %lld < 0", (long long)num_pairs);
+  if (num_pairs == 0) return PKV_OK;
+  PKV_TRY(check_ptr(src_dst_pairs, 8, "src_dst_pairs"));
+  PKV_TRY(check_ptr(k_cache, 16, "k_cache"));
+  PKV_TRY(check_ptr(v_cache, 16, "v_cache"));
+  unsigned* err = nullptr;
+  PKV_TRY(error_word(&err));
+  const int64_t block_bytes = static_cast<int64_t>(cache->block_size) * cache->num_kv_heads *
+                              cache->head_dim * elem_bytes(cache->dtype);
+  hipError_t e = pkv::launch_block_copy(k_cache, v_cache, src_dst_pairs, num_pairs,
+                                        cache->num_blocks, block_bytes, err,
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "block_copy launch");
+}
+
+size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                     int32_t max_blocks_per_seq, int32_t block_size,
+                                     int32_t partition_tokens) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
+      block_size <= 0)
+    return 0;
+  int32_t part = 0;
+  if (resolve_partition(partition_tokens, block_size, &part) != PKV_OK) return 0;
+  const int64_t max_tokens = static_cast<int64_t>(max_blocks_per_seq) * block_size;
+  const int64_t max_parts = (max_tokens + part - 1) / part;
+  if (max_parts <= 1) return 0;
+  return pkv::workspace_layout(num_seqs, num_q_heads, head_dim, max_parts).total;
+}
+
+int pkv_attention_decode(void* out, int32_t out_dtype, const void* q, const void* k_cache,
+                         const void* v_cache, const pkv_cache_desc* cache,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                         float scale, int32_t partition_tokens, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  PKV_TRY(check_cache(cache));
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
+  if (num_seqs > 65535) return fail(PKV_ERR_INVALID_ARG, "num_seqs %d > 65535", num_seqs);
+  if (num_q_heads < 1 || num_q_heads % cache->num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                num_q_heads, cache->num_kv_heads);
+  const int group = num_q_heads / cache->num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return fail(PKV_ERR_UNSUPPORTED, "query group %d is not 1, 2, 4 or 8", group);
+  if (out_dtype != PKV_F32 && out_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "out_dtype %d is neither PKV_F32 nor PKV_BF16", out_dtype);
+  if (max_blocks_per_seq < 1)
+    return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq %d < 1", max_blocks_per_seq);
+  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
+    return fail(PKV_ERR_INVALID_ARG, "scale is not finite");
+  int32_t part = 0;
+  PKV_TRY(resolve_partition(partition_tokens, cache->block_size, &part));
+  if (num_seqs == 0) return PKV_OK;
+  PKV_TRY(check_ptr(out, 16, "out"));
+  PKV_TRY(check_ptr(q, 16, "q"));
+  PKV_TRY(check_ptr(k_cache, 16, "k_cache"));
+  PKV_TRY(check_ptr(v_cache, 16, "v_cache"));
+  PKV_TRY(check_ptr(block_tables, 4, "block_tables"));
+  PKV_TRY(check_ptr(seq_lens, 4, "seq_lens"));
+  if (cache->num_blocks < 1) return fail(PKV_ERR_INVALID_ARG, "num_blocks must be >= 1");
+
+  const int64_t max_tokens = static_cast<int64_t>(max_blocks_per_seq) * cache->block_size;
+  if (max_tokens > 0x7FFFFFFF)
+    return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq * block_size exceeds 2^31 - 1");
+  const int64_t max_parts = (max_tokens + part - 1) / part;
+  if (max_parts > 65535)
+    return fail(PKV_ERR_INVALID_ARG, "%lld partitions per sequence exceed 65535", (long long)max_parts);
+
+  pkv::DecodeArgs a{};
+  if (max_parts > 1) {
+    const pkv::WorkspaceLayout lay =
+        pkv::workspace_layout(num_seqs, num_q_heads, cache->head_dim, max_parts);
+    if (!workspace)
+      return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", lay.total);
+    if (!aligned(workspace, 16)) return fail(PKV_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    if (workspace_bytes < lay.total)
+      return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", lay.total,
+                  workspace_bytes);
+    char* w = static_cast<char*>(workspace);
+    a.ws_max = reinterpret_cast<float*>(w + lay.max_off);
+    a.ws_sum = reinterpret_cast<float*>(w + lay.sum_off);
+    a.ws_acc = reinterpret_cast<float*>(w + lay.acc_off);
+  }
+  unsigned* err = nullptr;
+  PKV_TRY(error_word(&err));
+
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.err = err;
+  a.num_blocks = cache->num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.part_tokens = part;
+  a.max_parts = static_cast<int32_t>(max_parts);
+  a.out_bf16 = out_dtype == PKV_BF16;
+  a.scale_log2e = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
+
+  hipError_t e = pkv::launch_decode(a, cache->dtype == PKV_BF16, cache->head_dim,
+                                    cache->block_size, group, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "attention_decode launch");
+}
+
+int pkv_check_device_errors(void* stream) {
+  g_last_error.clear();
+  unsigned* err = nullptr;
+  PKV_TRY(error_word(&err));
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  unsigned word = 0;
+  e = hipMemcpy(&word, err, sizeof(word), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy(error word)");
+  if (word == 0) return PKV_OK;
+  const unsigned zero = 0;
+  e = hipMemcpy(err, &zero, sizeof(zero), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy(clear error word)");
+  return fail(PKV_ERR_INVALID_ARG, "device range checks failed:%s%s%s%s",
+              (word & pkv::kErrSlot) ? " slot>=num_blocks*block_size" : "",
+              (word & pkv::kErrBlockId) ? " block_id_out_of_range" : "",
+              (word & pkv::kErrSeqLen) ? " seq_len_out_of_range" : "",
+              (word & pkv::kErrCopyPair) ? " copy_pair_out_of_range" : "");
+}
+
+}  // extern "C"

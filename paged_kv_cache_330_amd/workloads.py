@@ -171,13 +171,23 @@ def make_decode_workload(config: int, *, block_size: Optional[int] = None,
                          num_seqs: Optional[int] = None,
                          seq_lens: Optional[Sequence[int]] = None,
                          seed: Optional[int] = None,
-                         table_pad: int = 0) -> DecodeWorkload:
+                         table_pad: int = 0,
+                         heads: Optional[Sequence[int]] = None,
+                         head_dim: Optional[int] = None,
+                         dtype: Optional[str] = None) -> DecodeWorkload:
     """Build decode workload ``config`` (1-4), optionally resized.
 
     ``seq_lens`` replaces the length draw (the draw is still made so that the
-    later draws do not move); ``num_seqs`` changes the batch.
+    later draws do not move); ``num_seqs`` changes the batch; ``heads``
+    (q heads, kv heads), ``head_dim`` and ``dtype`` reshape it for parity cases.
     """
     spec = CONFIGS[config]
+    if heads is not None or head_dim is not None or dtype is not None:
+        import dataclasses
+        hq, hkv = heads if heads is not None else (spec.num_q_heads, spec.num_kv_heads)
+        spec = dataclasses.replace(spec, num_q_heads=int(hq), num_kv_heads=int(hkv),
+                                   head_dim=spec.head_dim if head_dim is None else int(head_dim),
+                                   dtype=spec.dtype if dtype is None else dtype)
     if spec.lengths == "prefix":
         raise ValueError("use PrefixSharingWorkload for the prefix-sharing workload")
     bs = spec.block_size if block_size is None else int(block_size)
@@ -358,3 +368,32 @@ class PrefixSharingWorkload:
         shape = (self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim)
         val = 0x7FC0 if fill == "nan" else 0
         return np.full(shape, val, np.uint16), np.full(shape, val, np.uint16)
+
+
+# ---------------------------------------------------------------------------- device upload
+def torch_tensor(a: np.ndarray, dtype: str, device):
+    """Host array -> device tensor; bf16 bit patterns become torch.bfloat16 bit for bit."""
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)
+
+
+def empty_device_caches(num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
+                        dtype: str, device, fill: str = "nan"):
+    """Device K and V pools filled with NaN (bf16 0x7FC0 / fp32 0x7FC00000) or zeros."""
+    import torch
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    val = float("nan") if fill == "nan" else 0.0
+    shape = (num_blocks, block_size, num_kv_heads, head_dim)
+    return torch.full(shape, val, dtype=tdt, device=device), torch.full(shape, val, dtype=tdt, device=device)
+
+
+def host_bits(t) -> np.ndarray:
+    """Device tensor -> host array in the oracle's storage convention (uint16 for bf16)."""
+    import torch
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
