@@ -50,11 +50,27 @@ __all__ = [
 def bf16_round(x) -> np.ndarray:
     """binary32 -> bfloat16 bit patterns (uint16), round to nearest even.
 
-    Input generation only.  The inputs never hold NaN or infinity.
+    Input generation only.  The inputs never hold NaN or infinity.  Works in
+    chunks with in-place integer steps so that the full-size pools (10^9
+    values) round in seconds.
     """
-    bits = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    bias = ((bits >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
-    return ((bits + bias) >> np.uint32(16)).astype(np.uint16)
+    src = np.ascontiguousarray(x, dtype=np.float32)
+    flat = src.reshape(-1).view(np.uint32)
+    out = np.empty(flat.shape, dtype=np.uint16)
+    tmp = np.empty(min(flat.size, _CHUNK), dtype=np.uint32)
+    for s in range(0, flat.size, _CHUNK):
+        bits = flat[s:s + _CHUNK]
+        t = tmp[:bits.size]
+        np.right_shift(bits, 16, out=t)
+        np.bitwise_and(t, 1, out=t)
+        np.add(t, 0x7FFF, out=t)
+        np.add(t, bits, out=t)
+        np.right_shift(t, 16, out=t)
+        out[s:s + _CHUNK] = t
+    return out.reshape(src.shape)
+
+
+_CHUNK = 1 << 22
 
 
 @dataclass(frozen=True)
@@ -85,8 +101,19 @@ CONFIGS: Dict[int, ConfigSpec] = {
 
 
 def _normal(rng, shape, dtype: str) -> np.ndarray:
-    x = rng.standard_normal(shape, dtype=np.float32)
-    return x if dtype == "f32" else bf16_round(x)
+    """binary32 standard normal draws, rounded to bfloat16 for ``"bf16"``.
+
+    Drawn in consecutive chunks from ``rng``; the values equal those of one
+    ``rng.standard_normal(shape, dtype=np.float32)`` call.
+    """
+    if dtype == "f32":
+        return rng.standard_normal(shape, dtype=np.float32)
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    for s in range(0, n, _CHUNK):
+        m = min(_CHUNK, n - s)
+        out[s:s + m] = bf16_round(rng.standard_normal(m, dtype=np.float32))
+    return out.reshape(shape)
 
 
 def _draw_lengths(spec: ConfigSpec, rng, num_seqs: int) -> np.ndarray:
@@ -292,10 +319,10 @@ class PrefixSharingWorkload:
         rng = np.random.default_rng(seed)
         self._order = rng.permutation(self.num_blocks)
         Hkv, D = num_kv_heads, head_dim
-        self.prefix_k = bf16_round(rng.standard_normal((prompts, prefix_len, Hkv, D), dtype=np.float32))
-        self.prefix_v = bf16_round(rng.standard_normal((prompts, prefix_len, Hkv, D), dtype=np.float32))
-        self.tail_k = bf16_round(rng.standard_normal((self.num_seqs, tail_len, Hkv, D), dtype=np.float32))
-        self.tail_v = bf16_round(rng.standard_normal((self.num_seqs, tail_len, Hkv, D), dtype=np.float32))
+        self.prefix_k = _normal(rng, (prompts, prefix_len, Hkv, D), "bf16")
+        self.prefix_v = _normal(rng, (prompts, prefix_len, Hkv, D), "bf16")
+        self.tail_k = _normal(rng, (self.num_seqs, tail_len, Hkv, D), "bf16")
+        self.tail_v = _normal(rng, (self.num_seqs, tail_len, Hkv, D), "bf16")
         self.width = math.ceil((prefix_len + tail_len) / block_size)
         self.reset()
 
