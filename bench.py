@@ -4,7 +4,8 @@
 
 A step is one pass of the hot path over one batch: the slot-mapping write of
 every sequence's new token (pkv_kv_write), then decode attention over all
-cached tokens (pkv_attention_decode: main kernel + split-K reduce).  The
+cached tokens (pkv_attention_decode: the balanced-schedule kernel and the
+reduce of the sequences it cuts).  The
 default workload is the batch-256 Llama-3-8B-shaped GQA decode (32 q / 8 kv
 heads, head_dim 128, block_size 16, lognormal lengths, median 1024, clipped to
 [16, 8192]; seed 3), synthetic bf16 data resident in HBM.
@@ -125,6 +126,29 @@ def cpu_baseline(w, budget_s):
     }
 
 
+COUNTERS = os.path.join(ROOT, "profiles", "decode_balanced_llama3_8b_gqa_b256_hbm_counters.md")
+
+
+def measured_traffic():
+    """HBM bytes per decode call from the committed counter summary, or None.
+
+    The summary records the sha256 of the library sources it was taken with;
+    when the sources have changed since, the figure no longer describes the
+    kernels and None is returned.
+    """
+    import re
+    from paged_kv_cache_330_amd.build import source_digest
+    try:
+        text = open(COUNTERS).read()
+    except OSError:
+        return None
+    sha = re.search(r"kernel_sources_sha256:\s*([0-9a-f]{64})", text)
+    val = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
+    if not sha or not val or sha.group(1) != source_digest():
+        return None
+    return int(val.group(1))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -168,7 +192,8 @@ def main():
     bt = torch.from_numpy(w.block_tables).to(dev)
     sl = torch.from_numpy(w.seq_lens).to(dev)
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
-    ws_bytes = ops.pkv_attention_workspace_bytes(B, Hq, D, bt.shape[1], bs, args.partition_tokens)
+    ws_bytes = ops.pkv_attention_workspace_bytes(pools[0][0], pools[0][1], B, Hq, bt.shape[1],
+                                                 args.partition_tokens)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     ops.pkv_check_device_errors()
 
@@ -231,7 +256,9 @@ def main():
             "workload": w.name, "num_seqs": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
             "head_dim": D, "block_size": bs, "seq_len_sum": total_tokens,
             "seq_len_max": int(w.seq_lens.max()), "seq_len_min": int(w.seq_lens.min()),
-            "partition_tokens": args.partition_tokens or 512, "num_blocks": w.num_blocks,
+            "schedule": ("balanced" if args.partition_tokens == 0 else
+                         f"partitions of {args.partition_tokens} tokens"),
+            "num_blocks": w.num_blocks,
             "kv_pool_copies": len(pools), "seed": w.seed, "out_dtype": "f32",
         },
         "hbm_frac_step": round(value / HBM_PEAK_GBPS, 4),
@@ -247,13 +274,15 @@ def main():
         "attn_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 3),
         "kv_bytes_per_step": kv_bytes,
         "roofline": {
-            "kernel": "pkv_attention_decode (decode_mfma_kernel + splitk_reduce_kernel)",
+            "kernel": ("pkv_attention_decode: " + ("decode_balanced_kernel + balanced_reduce_kernel"
+                       if args.partition_tokens == 0 else "decode_mfma_kernel + splitk_reduce_kernel")),
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": (measured_traffic() if (args.config, args.block_size,
+                                                 args.partition_tokens) == (3, None, 0) else None),
             "algorithmic_bytes_per_launch": attn_alg_bytes,
         },
         "workload_gen_s": round(t_gen, 2),

@@ -91,13 +91,14 @@ int pkv_block_copy(void* k_cache, void* v_cache, const pkv_cache_desc* cache,
                    const int64_t* src_dst_pairs, int64_t num_pairs, void* stream);
 
 /*
- * Bytes of device workspace pkv_attention_decode needs for these sizes: the
- * per-partition partial results (running max, running sum and unnormalised
- * output, fp32) of the split-K decomposition.  0 when every sequence fits in
- * one partition.  partition_tokens 0 selects the default (512).
+ * Bytes of device workspace pkv_attention_decode needs for these sizes (0 when
+ * none is needed); the arguments mean what they mean for that call.  Returns
+ * 0 as well for arguments the call would reject (pkv_last_error() then says
+ * why).  Depends on host-known sizes only, so it can size a buffer before any
+ * sequence length is known.
  */
-size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                     int32_t max_blocks_per_seq, int32_t block_size,
+size_t pkv_attention_workspace_bytes(const pkv_cache_desc* cache, int32_t num_seqs,
+                                     int32_t num_q_heads, int32_t max_blocks_per_seq,
                                      int32_t partition_tokens);
 
 /*
@@ -108,8 +109,9 @@ size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int3
  * kv = h / G (consecutive grouping):
  *     out[b][h] = sum_t softmax_t(scale * <q[b][h], K_t>) * V_t
  * over the t < seq_lens[b] tokens reached through block_tables[b].
- * The sum runs over partitions of partition_tokens tokens whose partial
- * results are merged by max/sum rescaling.
+ * The tokens are split into pieces whose partial results (running max, sum
+ * of exponentials, unnormalised output) are merged by max/sum rescaling; the
+ * split changes the result only by fp32 rounding.
  *
  *   out           [num_seqs][num_q_heads][head_dim], out_dtype (PKV_F32 or
  *                 PKV_BF16, round to nearest even), written.  A sequence of
@@ -120,9 +122,15 @@ size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int3
  *   seq_lens      [num_seqs] int32, tokens cached for each sequence (the
  *                 newest included); must be <= max_blocks_per_seq*block_size.
  *   scale         softmax scale applied to the fp32 dot products.
- *   partition_tokens  0 (default 512) or a multiple of 64 and of block_size.
- *   workspace     pkv_attention_workspace_bytes(...) bytes (may be NULL when
- *                 that is 0), overwritten.
+ *   partition_tokens  0 chooses the split: for bf16 pools with head_dim 128
+ *                 and at most 2048 sequences, a balanced schedule that gives
+ *                 every workgroup an equal share of all the sequences' tokens;
+ *                 otherwise partitions of 512 tokens.  A positive value asks
+ *                 for partitions of that many tokens: a multiple of 64 and of
+ *                 block_size, at most 4096.
+ *   workspace     pkv_attention_workspace_bytes(...) bytes of scratch (may be
+ *                 NULL when that is 0), overwritten; calls that share a
+ *                 workspace must not overlap in time.
  * Pools, q, tables and lengths are only read.  num_seqs == 0 is a no-op.
  */
 int pkv_attention_decode(void* out, int32_t out_dtype, const void* q,

@@ -18,8 +18,26 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
-SOURCES = ["api.hip", "kv_write.hip", "block_copy.hip", "attention_decode.hip"]
+SOURCES = ["api.hip", "kv_write.hip", "block_copy.hip", "attention_mfma.hip", "attention_valu.hip"]
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
+
+
+def source_digest() -> str:
+    """sha256 over the library's sources (names and bytes, sorted by path).
+
+    Recorded next to the hardware-counter figures so that a reader, and the
+    benchmark, can tell whether those figures still describe the kernels.
+    """
+    import glob
+    import hashlib
+    files = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h")) +
+                   [os.path.join(ROOT, "include", "pagedkv.h")])
+    h = hashlib.sha256()
+    for f in sorted(files, key=lambda f: os.path.relpath(f, ROOT)):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def hipcc() -> str:

@@ -10,15 +10,14 @@
 
 namespace pkv {
 
-WorkspaceLayout workspace_layout(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim,
-                                 int64_t max_parts) {
+WorkspaceLayout workspace_layout(int64_t rows, int64_t head_dim, int64_t desc_ints) {
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
-  const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * max_parts;
   WorkspaceLayout l;
-  l.max_off = 0;
-  l.sum_off = up(rows * sizeof(float));
-  l.acc_off = l.sum_off + up(rows * sizeof(float));
-  l.total = l.acc_off + up(rows * head_dim * sizeof(float));
+  l.desc_off = 0;
+  l.max_off = up(static_cast<size_t>(desc_ints) * sizeof(int));
+  l.sum_off = l.max_off + up(static_cast<size_t>(rows) * sizeof(float));
+  l.acc_off = l.sum_off + up(static_cast<size_t>(rows) * sizeof(float));
+  l.total = l.acc_off + up(static_cast<size_t>(rows) * head_dim * sizeof(float));
   return l;
 }
 
@@ -99,11 +98,57 @@ int check_ptr(const void* p, size_t align, const char* name) {
 
 int resolve_partition(int32_t partition_tokens, int32_t block_size, int32_t* part) {
   const int32_t p = partition_tokens == 0 ? pkv::kDefaultPartitionTokens : partition_tokens;
-  if (p < 64 || p % 64 != 0 || p % block_size != 0)
+  if (p < 64 || p % 64 != 0 || p % block_size != 0 || p > pkv::kMaxPartitionTokens)
     return fail(PKV_ERR_INVALID_ARG,
-                "partition_tokens %d must be 0 or a positive multiple of 64 and of block_size %d",
-                partition_tokens, block_size);
+                "partition_tokens %d must be 0 or a multiple of 64 and of block_size %d, at most %d",
+                partition_tokens, block_size, pkv::kMaxPartitionTokens);
   *part = p;
+  return PKV_OK;
+}
+
+// Schedule and workspace of one decode call, from host-known sizes only.
+struct Plan {
+  int32_t part;       // partition grid: tokens per partition
+  int64_t max_parts;  // partition grid: partitions of the longest possible sequence
+  int32_t slices;     // > 0: balanced schedule, slices per kv head
+  pkv::WorkspaceLayout layout;
+  size_t workspace;   // bytes (0: none needed)
+};
+
+int make_plan(const pkv_cache_desc* cache, int32_t num_seqs, int32_t num_q_heads,
+              int32_t max_blocks_per_seq, int32_t partition_tokens, Plan* p) {
+  PKV_TRY(check_cache(cache));
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
+  if (num_seqs > 65535) return fail(PKV_ERR_INVALID_ARG, "num_seqs %d > 65535", num_seqs);
+  if (num_q_heads < 1 || num_q_heads % cache->num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                num_q_heads, cache->num_kv_heads);
+  if (max_blocks_per_seq < 1)
+    return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq %d < 1", max_blocks_per_seq);
+  const int64_t max_tokens = static_cast<int64_t>(max_blocks_per_seq) * cache->block_size;
+  if (max_tokens > 0x7FFFFFFF)
+    return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq * block_size exceeds 2^31 - 1");
+  PKV_TRY(resolve_partition(partition_tokens, cache->block_size, &p->part));
+  p->max_parts = (max_tokens + p->part - 1) / p->part;
+  if (p->max_parts > 65535)
+    return fail(PKV_ERR_INVALID_ARG, "%lld partitions per sequence exceed 65535",
+                (long long)p->max_parts);
+  // The balanced schedule serves the automatic choice for the bf16 head_dim
+  // 128 kernels; an explicit partition size asks for the partition grid.
+  const bool balanced = partition_tokens == 0 && cache->dtype == PKV_BF16 &&
+                        cache->head_dim == 128 && num_seqs <= pkv::kMaxBalancedSeqs &&
+                        num_seqs > 0;
+  p->slices = balanced ? pkv::balanced_slices(cache->num_kv_heads) : 0;
+  p->workspace = 0;
+  if (balanced) {
+    p->layout = pkv::workspace_layout(static_cast<int64_t>(p->slices) * 2 * num_q_heads,
+                                      cache->head_dim, 2 * static_cast<int64_t>(p->slices));
+    p->workspace = p->layout.total;
+  } else if (p->max_parts > 1 && num_seqs > 0) {
+    p->layout = pkv::workspace_layout(static_cast<int64_t>(num_seqs) * num_q_heads * p->max_parts,
+                                      cache->head_dim, 0);
+    p->workspace = p->layout.total;
+  }
   return PKV_OK;
 }
 
@@ -153,18 +198,13 @@ int pkv_block_copy(void* k_cache, void* v_cache, const pkv_cache_desc* cache,
   return e == hipSuccess ? PKV_OK : hip_fail(e, "block_copy launch");
 }
 
-size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                     int32_t max_blocks_per_seq, int32_t block_size,
+size_t pkv_attention_workspace_bytes(const pkv_cache_desc* cache, int32_t num_seqs,
+                                     int32_t num_q_heads, int32_t max_blocks_per_seq,
                                      int32_t partition_tokens) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
-      block_size <= 0)
+  Plan p;
+  if (make_plan(cache, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, &p) != PKV_OK)
     return 0;
-  int32_t part = 0;
-  if (resolve_partition(partition_tokens, block_size, &part) != PKV_OK) return 0;
-  const int64_t max_tokens = static_cast<int64_t>(max_blocks_per_seq) * block_size;
-  const int64_t max_parts = (max_tokens + part - 1) / part;
-  if (max_parts <= 1) return 0;
-  return pkv::workspace_layout(num_seqs, num_q_heads, head_dim, max_parts).total;
+  return p.workspace;
 }
 
 int pkv_attention_decode(void* out, int32_t out_dtype, const void* q, const void* k_cache,
@@ -174,23 +214,15 @@ int pkv_attention_decode(void* out, int32_t out_dtype, const void* q, const void
                          float scale, int32_t partition_tokens, void* workspace,
                          size_t workspace_bytes, void* stream) {
   g_last_error.clear();
-  PKV_TRY(check_cache(cache));
-  if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
-  if (num_seqs > 65535) return fail(PKV_ERR_INVALID_ARG, "num_seqs %d > 65535", num_seqs);
-  if (num_q_heads < 1 || num_q_heads % cache->num_kv_heads != 0)
-    return fail(PKV_ERR_INVALID_ARG, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
-                num_q_heads, cache->num_kv_heads);
+  Plan plan;
+  PKV_TRY(make_plan(cache, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, &plan));
   const int group = num_q_heads / cache->num_kv_heads;
   if (group != 1 && group != 2 && group != 4 && group != 8)
     return fail(PKV_ERR_UNSUPPORTED, "query group %d is not 1, 2, 4 or 8", group);
   if (out_dtype != PKV_F32 && out_dtype != PKV_BF16)
     return fail(PKV_ERR_UNSUPPORTED, "out_dtype %d is neither PKV_F32 nor PKV_BF16", out_dtype);
-  if (max_blocks_per_seq < 1)
-    return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq %d < 1", max_blocks_per_seq);
   if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
     return fail(PKV_ERR_INVALID_ARG, "scale is not finite");
-  int32_t part = 0;
-  PKV_TRY(resolve_partition(partition_tokens, cache->block_size, &part));
   if (num_seqs == 0) return PKV_OK;
   PKV_TRY(check_ptr(out, 16, "out"));
   PKV_TRY(check_ptr(q, 16, "q"));
@@ -200,27 +232,19 @@ int pkv_attention_decode(void* out, int32_t out_dtype, const void* q, const void
   PKV_TRY(check_ptr(seq_lens, 4, "seq_lens"));
   if (cache->num_blocks < 1) return fail(PKV_ERR_INVALID_ARG, "num_blocks must be >= 1");
 
-  const int64_t max_tokens = static_cast<int64_t>(max_blocks_per_seq) * cache->block_size;
-  if (max_tokens > 0x7FFFFFFF)
-    return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq * block_size exceeds 2^31 - 1");
-  const int64_t max_parts = (max_tokens + part - 1) / part;
-  if (max_parts > 65535)
-    return fail(PKV_ERR_INVALID_ARG, "%lld partitions per sequence exceed 65535", (long long)max_parts);
-
   pkv::DecodeArgs a{};
-  if (max_parts > 1) {
-    const pkv::WorkspaceLayout lay =
-        pkv::workspace_layout(num_seqs, num_q_heads, cache->head_dim, max_parts);
+  if (plan.workspace > 0) {
     if (!workspace)
-      return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", lay.total);
+      return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", plan.workspace);
     if (!aligned(workspace, 16)) return fail(PKV_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
-    if (workspace_bytes < lay.total)
-      return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", lay.total,
+    if (workspace_bytes < plan.workspace)
+      return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", plan.workspace,
                   workspace_bytes);
     char* w = static_cast<char*>(workspace);
-    a.ws_max = reinterpret_cast<float*>(w + lay.max_off);
-    a.ws_sum = reinterpret_cast<float*>(w + lay.sum_off);
-    a.ws_acc = reinterpret_cast<float*>(w + lay.acc_off);
+    a.ws_desc = reinterpret_cast<int*>(w + plan.layout.desc_off);
+    a.ws_max = reinterpret_cast<float*>(w + plan.layout.max_off);
+    a.ws_sum = reinterpret_cast<float*>(w + plan.layout.sum_off);
+    a.ws_acc = reinterpret_cast<float*>(w + plan.layout.acc_off);
   }
   unsigned* err = nullptr;
   PKV_TRY(error_word(&err));
@@ -237,8 +261,9 @@ int pkv_attention_decode(void* out, int32_t out_dtype, const void* q, const void
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = cache->num_kv_heads;
-  a.part_tokens = part;
-  a.max_parts = static_cast<int32_t>(max_parts);
+  a.part_tokens = plan.part;
+  a.max_parts = static_cast<int32_t>(plan.max_parts);
+  a.slices = plan.slices;
   a.out_bf16 = out_dtype == PKV_BF16;
   a.scale_log2e = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
 

@@ -17,6 +17,26 @@ enum : unsigned {
 };
 
 constexpr int kDefaultPartitionTokens = 512;
+constexpr int kMaxPartitionTokens = 4096;  // bounds the LDS window of block-table entries
+constexpr int kMaxBalancedSeqs = 2048;     // batch limit of the balanced schedule (LDS scan)
+
+// Build-time tuning of the bf16 decode kernels (defaults are the measured best).
+#ifndef PKV_MFMA_TILE_CHUNKS
+#define PKV_MFMA_TILE_CHUNKS 1  // 16-token chunks per wave tile
+#endif
+#ifndef PKV_BALANCED_WGS
+#define PKV_BALANCED_WGS 256    // workgroups of the balanced schedule (all kv-head groups)
+#endif
+
+// Waves per workgroup of the matrix-core kernels: one per kv head, the
+// largest of 8, 4, 2, 1 that divides num_kv_heads.
+int mfma_waves_per_group(int num_kv_heads);
+
+// Slices of the balanced schedule (per kv-head group).
+inline int balanced_slices(int num_kv_heads) {
+  const int groups = num_kv_heads / mfma_waves_per_group(num_kv_heads);
+  return (PKV_BALANCED_WGS + groups - 1) / groups;
+}
 
 // Everything one decode launch needs; passed by value as a kernel argument.
 struct DecodeArgs {
@@ -26,9 +46,13 @@ struct DecodeArgs {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* seq_lens;
-  float* ws_max;   // [B][Hq][max_parts]
-  float* ws_sum;   // [B][Hq][max_parts]
-  float* ws_acc;   // [B][Hq][max_parts][D]
+  // Partial results.  Partition grid: rows [B][Hq][max_parts].  Balanced
+  // schedule: rows [slices][Hkv][2][G] (slices per kv-head group).  acc rows
+  // hold D floats.
+  float* ws_max;
+  float* ws_sum;
+  float* ws_acc;
+  int* ws_desc;    // balanced schedule: per slice, (cut sequence ending there or -1, its first slice)
   unsigned* err;
   int64_t num_blocks;
   int32_t max_blocks_per_seq;
@@ -38,15 +62,17 @@ struct DecodeArgs {
   int32_t part_tokens;
   int32_t max_parts;
   int32_t out_bf16;
+  int32_t slices;      // > 0: balanced schedule with this many slices per kv head
   float scale_log2e;   // softmax scale * log2(e): scores feed exp2
 };
 
 // Workspace carve-up shared by the size query and the launch.
 struct WorkspaceLayout {
-  size_t max_off, sum_off, acc_off, total;
+  size_t desc_off, max_off, sum_off, acc_off, total;
 };
-WorkspaceLayout workspace_layout(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim,
-                                 int64_t max_parts);
+// Partition grid: `rows` = B * Hq * max_parts, no descriptors.  Balanced
+// schedule: `rows` = slices * 2 * Hq, `desc_ints` = 2 * slices.
+WorkspaceLayout workspace_layout(int64_t rows, int64_t head_dim, int64_t desc_ints);
 
 hipError_t launch_kv_write(const void* k, const void* v, const int64_t* slots, int64_t n,
                            void* k_cache, void* v_cache, int64_t num_slots, int64_t row_bytes,
@@ -56,10 +82,14 @@ hipError_t launch_block_copy(void* k_cache, void* v_cache, const int64_t* pairs,
                              int64_t num_pairs, int64_t num_blocks, int64_t block_bytes,
                              unsigned* err, hipStream_t stream);
 
-// Chooses the kernel for (dtype, head_dim, block_size, group) and launches the
-// main pass and, when max_parts > 1, the split-K reduce.  Returns
+// Chooses the kernel for (dtype, head_dim, block_size, group) and schedule
+// (a.slices > 0: balanced; else the partition grid) and launches the main
+// pass and, when partial results can exist, the matching reduce.  Returns
 // hipErrorInvalidValue for a combination that has no kernel.
-hipError_t launch_decode(const DecodeArgs& a, int bf16, int head_dim, int block_size,
-                         int group, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int bf16, int head_dim, int block_size, int group,
+                         hipStream_t stream);
+
+// The bf16 head_dim-128 kernels of either schedule (attention_mfma.hip).
+hipError_t launch_mfma_decode(const DecodeArgs& a, int block_size, int group, hipStream_t stream);
 
 }  // namespace pkv

@@ -69,7 +69,7 @@ def load_library() -> ctypes.CDLL:
     D = ctypes.POINTER(CacheDesc)
     lib.pkv_kv_write.argtypes = [P, P, P, I64, P, P, D, P]
     lib.pkv_block_copy.argtypes = [P, P, D, P, I64, P]
-    lib.pkv_attention_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
+    lib.pkv_attention_workspace_bytes.argtypes = [D, I32, I32, I32, I32]
     lib.pkv_attention_workspace_bytes.restype = SZ
     lib.pkv_attention_decode.argtypes = [P, I32, P, P, P, D, P, I32, P, I32, I32,
                                          ctypes.c_float, I32, P, SZ, P]
@@ -156,11 +156,13 @@ def pkv_block_copy(k_cache: torch.Tensor, v_cache: torch.Tensor,
                                          _ptr(src_dst_pairs), src_dst_pairs.shape[0], _stream()))
 
 
-def pkv_attention_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
-                                  max_blocks_per_seq: int, block_size: int,
+def pkv_attention_workspace_bytes(k_cache: torch.Tensor, v_cache: torch.Tensor, num_seqs: int,
+                                  num_q_heads: int, max_blocks_per_seq: int,
                                   partition_tokens: int = 0) -> int:
+    """Workspace bytes ``pkv_attention_decode`` needs for these pools and sizes."""
+    desc = _desc(k_cache, v_cache)
     return int(load_library().pkv_attention_workspace_bytes(
-        num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size, partition_tokens))
+        ctypes.byref(desc), num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens))
 
 
 def pkv_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
@@ -185,7 +187,8 @@ def pkv_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tens
     if block_tables.shape[0] != B or seq_lens.shape[0] != B:
         raise ValueError("block_tables/seq_lens must have B rows")
     mb = block_tables.shape[1]
-    need = pkv_attention_workspace_bytes(B, Hq, D, mb, desc.block_size, partition_tokens)
+    need = int(load_library().pkv_attention_workspace_bytes(
+        ctypes.byref(desc), B, Hq, mb, partition_tokens))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if workspace is not None:

@@ -104,8 +104,12 @@ def test_decode_validation(lib):
     assert decode(lib, B=-1) == INVALID
 
 
+def ws_bytes(lib, d, B, Hq, mb, part):
+    return lib.pkv_attention_workspace_bytes(ctypes.byref(d), B, Hq, mb, part)
+
+
 def test_decode_workspace_validation(lib):
-    need = lib.pkv_attention_workspace_bytes(4, 32, 128, 64, 16, 0)   # 1024 tokens: 2 partitions
+    need = ws_bytes(lib, desc(), 4, 32, 64, 0)
     assert need > 0
     assert decode(lib, mb=64, ws=P(0)) == WORKSPACE
     assert "required" in ops.pkv_last_error()
@@ -113,13 +117,40 @@ def test_decode_workspace_validation(lib):
     assert decode(lib, mb=64, ws=P(FAKE + 8)) == INVALID
 
 
-def test_workspace_size_formula(lib):
-    # One partition of 512 tokens per sequence needs no workspace.
-    assert lib.pkv_attention_workspace_bytes(256, 32, 128, 32, 16, 0) == 0
+def up(x):
+    return (x + 255) // 256 * 256
+
+
+def test_workspace_size_partition_grid(lib):
+    # An explicit partition size asks for the partition grid: one partition of
+    # 512 tokens per sequence needs no workspace.
+    assert ws_bytes(lib, desc(), 256, 32, 32, 512) == 0
     # 8192 tokens at 512 per partition: 16 partials of (max, sum, acc[128]) per row.
     rows = 256 * 32 * 16
-    got = lib.pkv_attention_workspace_bytes(256, 32, 128, 512, 16, 0)
-    assert got == 2 * rows * 4 + rows * 128 * 4
-    assert lib.pkv_attention_workspace_bytes(8, 64, 128, 1024, 32, 512) == \
-        2 * (8 * 64 * 64 * 4) + 8 * 64 * 64 * 128 * 4
-    assert lib.pkv_attention_workspace_bytes(8, 64, 128, 1024, 32, 100) == 0  # invalid partition
+    assert ws_bytes(lib, desc(), 256, 32, 512, 512) == 2 * rows * 4 + rows * 128 * 4
+    # fp32 pools take the partition grid for the automatic choice too (512 tokens).
+    assert ws_bytes(lib, desc(dtype=0), 256, 32, 512, 0) == 2 * rows * 4 + rows * 128 * 4
+    d32 = desc(bs=32, hkv=8)
+    assert ws_bytes(lib, d32, 8, 64, 1024, 512) == 2 * (8 * 64 * 64 * 4) + 8 * 64 * 64 * 128 * 4
+    assert ws_bytes(lib, d32, 8, 64, 1024, 100) == 0    # not a multiple of 64
+    assert ws_bytes(lib, d32, 8, 64, 1024, 8192) == 0   # above 4096
+    assert ws_bytes(lib, desc(), 0, 32, 512, 0) == 0     # empty batch
+
+
+def balanced_bytes(slices, hq, d=128):
+    # per slice: a merge descriptor (2 ints), then partials of (max, sum,
+    # acc[d]) for 2 pieces per (kv head, query head of its group)
+    return up(2 * slices * 4) + 2 * up(slices * 2 * hq * 4) + up(slices * 2 * hq * d * 4)
+
+
+def test_workspace_size_balanced_schedule(lib):
+    # bf16, head_dim 128, automatic choice; the size does not depend on B or
+    # on the table width, only on the number of slices.
+    got = ws_bytes(lib, desc(), 256, 32, 512, 0)
+    slices = next(s for s in range(1, 100000) if balanced_bytes(s, 32) >= got)
+    assert got == balanced_bytes(slices, 32)
+    assert slices >= 32                # every CU gets work at 8 waves per workgroup
+    assert ws_bytes(lib, desc(), 3, 32, 7, 0) == got
+    assert ws_bytes(lib, desc(), 2048, 32, 64, 0) == got
+    # beyond 2048 sequences the partition grid takes over
+    assert ws_bytes(lib, desc(), 4096, 32, 64, 0) == 2 * (4096 * 32 * 2 * 4) + 4096 * 32 * 2 * 128 * 4

@@ -111,15 +111,65 @@ SMALL_CASES = [
 
 
 # --------------------------------------------------------------------------- write / copy
+# partition_tokens 0 lets the library choose (the balanced schedule for bf16
+# head_dim 128, else 512-token partitions); 512 forces the partition grid.
+SCHEDULES = [0, 512]
+
+
+@pytest.mark.parametrize("schedule", SCHEDULES, ids=["auto", "grid512"])
 @pytest.mark.parametrize("case", SMALL_CASES, ids=[c[0] for c in SMALL_CASES])
-def test_write_then_decode_matches_oracle(ops, case):
+def test_write_then_decode_matches_oracle(ops, case, schedule):
     name, config, lens, bs, heads, hd, dt = case
-    say(f"case {name}")
+    say(f"case {name} schedule {schedule}")
     w = workload(config, lens, bs, heads, hd, dt)
-    kc, vc, out = gpu_step(ops, w)
+    kc, vc, out = gpu_step(ops, w, partition_tokens=schedule)
     rk, rv = oracle_caches(w)
     assert same_bits(kc, rk) and same_bits(vc, rv), "pool bytes differ"
     assert_close(out.cpu().numpy(), oracle_decode(w, rk, rv), TOL[w.dtype], name)
+
+
+BALANCED_CASES = [
+    # one long sequence cut into a piece per slice
+    ("one_long_seq", 3, (20000,), 16, None),
+    ("one_long_seq_bs64_gqa8", 4, (9000,), 64, None),
+    # many sequences per slice, one-token and chunk-edge lengths
+    ("many_short", 3, tuple([1, 2, 16, 17, 31, 33] * 60), 16, None),
+    ("mha_mixed", 2, (1, 5000, 16, 3000, 1, 7), 16, None),
+    ("bs8_mixed", 3, (700, 1, 9, 4100, 23), 8, None),
+]
+
+
+@pytest.mark.parametrize("case", BALANCED_CASES, ids=[c[0] for c in BALANCED_CASES])
+def test_balanced_schedule_edges(ops, case):
+    name, config, lens, bs, heads = case
+    say(f"balanced case {name}")
+    w = workload(config, lens, bs, heads)
+    kc, vc, out = gpu_step(ops, w)
+    rk, rv = oracle_caches(w)
+    rows = sorted({0, len(lens) - 1, int(np.argmax(w.seq_lens)), len(lens) // 2})
+    assert_close(out.cpu().numpy()[rows], oracle_decode(w, rk, rv, rows), TOL["bf16"], name)
+
+
+def test_balanced_schedule_zero_lengths_and_large_batch(ops):
+    # zero-length rows inside a balanced batch, and a batch above the balanced
+    # limit (2048 sequences) that falls back to the partition grid
+    for lens in ((0, 40, 0, 900, 0), (3,) * 2100):
+        w = workload(3, tuple(max(1, L) for L in lens), 16)
+        kc, vc, out = gpu_step(ops, w)
+        sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        out2 = torch.full_like(out, 7.0)
+        ops.pkv_attention_decode(out2, torch_tensor(w.q, "bf16", "cuda"), kc, vc,
+                                 torch.from_numpy(w.block_tables).cuda(), sl, float(w.scale))
+        ops.pkv_check_device_errors()
+        rk, rv = oracle_caches(w)
+        rows = [i for i, L in enumerate(lens) if L > 0][:8]
+        ref = oracle.decode_ref(w.q[rows], rk, rv, w.block_tables[rows], np.array(lens, np.int32)[rows],
+                                w.scale, "bf16")
+        got = out2.cpu().numpy()
+        assert_close(got[rows], ref, TOL["bf16"], f"batch {len(lens)}")
+        for i, L in enumerate(lens):
+            if L == 0:
+                assert (got[i] == 0).all()
 
 
 def test_write_skips_negative_slots(ops):
