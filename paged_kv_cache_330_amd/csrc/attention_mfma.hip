@@ -53,6 +53,13 @@ namespace {
 constexpr int kD = 128;
 constexpr int kMaxWaves = 8;
 
+#if PKV_BALANCED_WAVES_PER_EU > 0
+#define PKV_BALANCED_OCCUPANCY \
+  __attribute__((amdgpu_waves_per_eu(PKV_BALANCED_WAVES_PER_EU, PKV_BALANCED_WAVES_PER_EU)))
+#else
+#define PKV_BALANCED_OCCUPANCY
+#endif
+
 // K and V rows of one tile (TC chunks of 16 tokens) of one wave.
 template <int TC>
 struct KVTile {
@@ -70,6 +77,16 @@ struct TileCtx {
   int last_chunk;         // start of the window's last 16-token chunk
   int col, qr;
 };
+
+// 16 bytes of a K or V row; every K/V byte is read once per call, so the
+// loads may carry the streaming (non-temporal) hint.
+__device__ __forceinline__ u32x4_t load_kv(const uint16_t* p) {
+#if PKV_KV_NONTEMPORAL
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+#else
+  return *reinterpret_cast<const u32x4_t*>(p);
+#endif
+}
 
 // Issue the loads of the tile starting at token t0.  Chunks past the end of
 // the window re-read its last chunk and tokens past the end re-read its last
@@ -94,12 +111,12 @@ __device__ __forceinline__ void load_tile(KVTile<TC>& r, int t0, const TileCtx& 
     }
     const uint16_t* kp = c.kbase + ((int64_t)pk * BS + (tk & (BS - 1))) * c.tok_stride;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) r.k[ch][s] = *reinterpret_cast<const u32x4_t*>(kp + 32 * s);
+    for (int s = 0; s < 4; ++s) r.k[ch][s] = load_kv(kp + 32 * s);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tv = min(tce + 4 * c.qr + i, c.end - 1);
       const uint16_t* vp = c.vbase + ((int64_t)pv[i] * BS + (tv & (BS - 1))) * c.tok_stride;
-      r.v[ch][i] = *reinterpret_cast<const u32x4_t*>(vp);
+      r.v[ch][i] = load_kv(vp);
     }
   }
 }
@@ -198,21 +215,35 @@ __device__ __forceinline__ void stream_window(const DecodeArgs& a, const TileCtx
   int t0 = begin;
   KVTile<TC> cur;
   load_tile<BS, TC>(cur, t0, c);
-  // The first tile passes through an empty asm so that the loop-carried
-  // `cur` is not a load on every incoming edge: otherwise the optimiser
-  // merges the two loads into one at the loop top, which undoes the prefetch.
-  // (It waits for the first tile, which is needed next anyway.)
+#if PKV_PREFETCH_TILES >= 2
+  KVTile<TC> n1;
+  load_tile<BS, TC>(n1, t0 + TILE, c);
+#endif
+  // The first tile(s) pass through an empty asm so that the loop-carried
+  // buffers are not loads on every incoming edge: otherwise the optimiser
+  // merges the loads into one at the loop top, which undoes the prefetch.
+  // (It waits for the first tile(s), which are needed next anyway.)
 #pragma unroll
   for (int ch = 0; ch < TC; ++ch)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(cur.k[ch][s]), "+v"(cur.v[ch][s]));
+    for (int s = 0; s < 4; ++s) {
+      asm volatile("" : "+v"(cur.k[ch][s]), "+v"(cur.v[ch][s]));
+#if PKV_PREFETCH_TILES >= 2
+      asm volatile("" : "+v"(n1.k[ch][s]), "+v"(n1.v[ch][s]));
+#endif
+    }
   while (true) {
     KVTile<TC> nxt;
-    load_tile<BS, TC>(nxt, t0 + TILE, c);
+    load_tile<BS, TC>(nxt, t0 + PKV_PREFETCH_TILES * TILE, c);
     compute_tile<G, TC>(cur, t0, c.end, qop, a.scale_log2e, c.qr, st);
     t0 += TILE;
     if (t0 >= c.end) break;
+#if PKV_PREFETCH_TILES >= 2
+    cur = n1;
+    n1 = nxt;
+#else
     cur = nxt;
+#endif
   }
 }
 
@@ -365,7 +396,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mfma_kernel(DecodeArgs 
 // sequence and the slice of its first piece, or -1.
 // ----------------------------------------------------------------------------
 template <int G, int BS, int TC>
-__global__ __launch_bounds__(kMaxWaves * 64) void decode_balanced_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kMaxWaves * 64) PKV_BALANCED_OCCUPANCY void decode_balanced_kernel(
+    DecodeArgs a) {
   static_assert(16 % G == 0, "group must divide 16");
   __shared__ int s_bt[kMaxPartitionTokens / BS + 1];
   __shared__ int s_cc[kMaxBalancedSeqs + 1];
