@@ -70,6 +70,8 @@ struct KVTile {
 struct TileCtx {
   const uint16_t* kbase;  // K pool + kv head offset + this lane's d-chunk
   const uint16_t* vbase;  // V pool + kv head offset + this lane's dims
+  const uint16_t* kdead;  // this wave's query row + this lane's d-chunk (see load_tile)
+  const uint16_t* vdead;  // this wave's query row + this lane's dims
   int64_t tok_stride;     // elements between consecutive slots
   const int* s_bt;        // physical block ids of the window (LDS)
   int blk0;               // logical block of s_bt[0]
@@ -88,14 +90,17 @@ __device__ __forceinline__ u32x4_t load_kv(const uint16_t* p) {
 #endif
 }
 
-// Issue the loads of the tile starting at token t0.  Chunks past the end of
-// the window re-read its last chunk and tokens past the end re-read its last
-// token, so every address is a valid row (the scores of such tokens are
-// masked to -inf).
+// Issue the loads of the tile starting at token t0.  Tokens past the end of
+// the window re-read its last token, so every address is a valid row (the
+// scores of such tokens are masked to -inf).  A chunk wholly past the end
+// (the prefetch after a window's last tile, never computed) reads this
+// wave's 256-byte query row instead, which is in cache, so it costs no HBM
+// traffic.
 template <int BS, int TC>
 __device__ __forceinline__ void load_tile(KVTile<TC>& r, int t0, const TileCtx& c) {
 #pragma unroll
   for (int ch = 0; ch < TC; ++ch) {
+    const bool dead = t0 + 16 * ch > c.last_chunk;
     const int tce = min(t0 + 16 * ch, c.last_chunk);
     const int tk = min(tce + c.col, c.end - 1);
     int pk, pv[4];
@@ -109,13 +114,15 @@ __device__ __forceinline__ void load_tile(KVTile<TC>& r, int t0, const TileCtx& 
 #pragma unroll
       for (int i = 0; i < 4; ++i) pv[i] = c.s_bt[min(tce + 4 * c.qr + i, c.end - 1) / BS - c.blk0];
     }
-    const uint16_t* kp = c.kbase + ((int64_t)pk * BS + (tk & (BS - 1))) * c.tok_stride;
+    const uint16_t* kp =
+        dead ? c.kdead : c.kbase + ((int64_t)pk * BS + (tk & (BS - 1))) * c.tok_stride;
 #pragma unroll
     for (int s = 0; s < 4; ++s) r.k[ch][s] = load_kv(kp + 32 * s);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tv = min(tce + 4 * c.qr + i, c.end - 1);
-      const uint16_t* vp = c.vbase + ((int64_t)pv[i] * BS + (tv & (BS - 1))) * c.tok_stride;
+      const uint16_t* vp =
+          dead ? c.vdead : c.vbase + ((int64_t)pv[i] * BS + (tv & (BS - 1))) * c.tok_stride;
       r.v[ch][i] = load_kv(vp);
     }
   }
@@ -257,12 +264,16 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, int* s_bt, int
                                              WaveState<G>& st) {
   const int lane = threadIdx.x & 63;
   const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
+  const uint16_t* qrow =
+      static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.num_q_heads + kvh * G) * kD;
   TileCtx c;
   c.tok_stride = (int64_t)a.num_kv_heads * kD;
   c.col = lane & 15;
   c.qr = lane >> 4;
   c.kbase = static_cast<const uint16_t*>(a.k_cache) + (int64_t)kvh * kD + 8 * c.qr;
   c.vbase = static_cast<const uint16_t*>(a.v_cache) + (int64_t)kvh * kD + 8 * c.col;
+  c.kdead = qrow + 8 * c.qr;  // + 32 s: 16 bytes inside the 128-element row
+  c.vdead = qrow + 8 * c.col;
   c.s_bt = s_bt;
   for (int w0 = begin; w0 < end; w0 += kMaxPartitionTokens) {
     const int wend = min(end, w0 + kMaxPartitionTokens);
