@@ -1,23 +1,28 @@
 """Benchmark of the paged decode step on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--config 3] [--block-size BS]
+    python bench.py --report-all      # one line per workload, then the metric line
+    python bench.py --read-probe      # plain streaming read: the practical HBM rate
+    python bench.py --copy-probe      # 1 GiB device copy (counter calibration)
 
 A step is one pass of the hot path over one batch: the slot-mapping write of
 every sequence's new token (pkv_kv_write), then decode attention over all
 cached tokens (pkv_attention_decode: the balanced-schedule kernel and the
-reduce of the sequences it cuts).  The
+reduce of the sequences it cuts).  For the prefix-sharing workload the step
+also holds the copy-on-write block copies of its first divergent step.  The
 default workload is the batch-256 Llama-3-8B-shaped GQA decode (32 q / 8 kv
 heads, head_dim 128, block_size 16, lognormal lengths, median 1024, clipped to
 [16, 8192]; seed 3), synthetic bf16 data resident in HBM.
 
 Cache honesty: the step rotates over several identical copies of the KV pool
 (--pools, default 3), so that no step finds the previous step's blocks in the
-L2 / MALL caches.
+L2 / MALL caches (the prefix-sharing pool, 67 MB of unique K/V, is
+cache-resident by nature and is reported as such).
 
-Prints one JSON line: value = KV GB/s of the whole step (KV bytes the step's
-attention must read / step time), plus the attention-only rate, tokens/s, a
-roofline entry for the decode call and the fp64 CPU oracle timed on a bounded
-sample of the same workload.
+The default run prints one JSON line: value = KV GB/s of the whole step (KV
+bytes the step's attention must read / step time), plus the attention-only
+rate, tokens/s, a roofline entry for the decode call and the fp64 CPU oracle
+timed on a bounded sample of the same workload.
 """
 import argparse
 import json
@@ -32,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "paged decode attn KV GB/s (% of HBM peak) + tokens/s, GQA batch 256"
+COUNTERS = os.path.join(ROOT, "profiles", "decode_balanced_llama3_8b_gqa_b256_hbm_counters.md")
 
 
 def parse():
@@ -43,9 +49,14 @@ def parse():
     p.add_argument("--block-size", type=int, default=None)
     p.add_argument("--partition-tokens", type=int, default=0)
     p.add_argument("--pools", type=int, default=3)
+    p.add_argument("--prefix", type=int, default=2044, help="prefix-sharing workload: prompt tokens")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate budget of the CPU oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--report-all", action="store_true",
+                   help="one line per workload (config 2, 4 at bs 32/64, 5 at bs 8/16), then the metric line")
+    p.add_argument("--read-probe", action="store_true",
+                   help="only time a plain streaming read of 4 GiB (context for the roofline)")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device copy (HBM counter calibration)")
     return p.parse_args()
@@ -59,6 +70,56 @@ def copy_probe(torch):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+
+
+def read_probe(torch):
+    """Plain streaming read of 4 GiB with the streaming hint, several grid sizes."""
+    import ctypes
+    from paged_kv_cache_330_amd.build import PROBE_LIB
+    if not os.path.exists(PROBE_LIB):
+        raise RuntimeError(f"{PROBE_LIB} is missing: build with `python -m paged_kv_cache_330_amd.build`")
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.pkv_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                          ctypes.c_int, ctypes.c_void_p]
+    buf = torch.ones(4 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for blocks in (8192, 16384, 32768, 65536):
+        ts = []
+        for _ in range(12):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if lib.pkv_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), buf.numel(),
+                                         ctypes.c_void_p(sink.data_ptr()), blocks, stream) != 0:
+                raise RuntimeError("stream probe launch failed")
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        res[blocks] = round(buf.numel() / (statistics.median(ts[2:]) * 1e-3) / 1e9, 1)
+    print(json.dumps({"read_probe_bytes": buf.numel(), "gbps_by_workgroups": res,
+                      "best_gbps": max(res.values()),
+                      "best_frac_of_peak": round(max(res.values()) / HBM_PEAK_GBPS, 4)}), flush=True)
+
+
+def measured_traffic():
+    """HBM bytes per decode call from the committed counter summary, or None.
+
+    The summary records the sha256 of the library sources it was taken with;
+    when the sources have changed since, the figure no longer describes the
+    kernels and None is returned.
+    """
+    import re
+    from paged_kv_cache_330_amd.build import source_digest
+    try:
+        text = open(COUNTERS).read()
+    except OSError:
+        return None
+    sha = re.search(r"kernel_sources_sha256:\s*([0-9a-f]{64})", text)
+    val = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
+    if not sha or not val or sha.group(1) != source_digest():
+        return None
+    return int(val.group(1))
 
 
 def cpu_baseline(w, budget_s):
@@ -126,27 +187,187 @@ def cpu_baseline(w, budget_s):
     }
 
 
-COUNTERS = os.path.join(ROOT, "profiles", "decode_balanced_llama3_8b_gqa_b256_hbm_counters.md")
+# --------------------------------------------------------------------------- device state
+class Step:
+    """Device tensors of one decode step and the phases that run it."""
+
+    def __init__(self, torch, ops, pools, q, bt, sl, k_new, v_new, slots, pairs, scale,
+                 partition_tokens):
+        self.torch, self.ops = torch, ops
+        self.pools, self.q, self.bt, self.sl = pools, q, bt, sl
+        self.k_new, self.v_new, self.slots, self.pairs = k_new, v_new, slots, pairs
+        self.scale, self.part = scale, partition_tokens
+        B, Hq, D = q.shape
+        kc, vc = pools[0]
+        self.out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+        need = ops.pkv_attention_workspace_bytes(kc, vc, B, Hq, bt.shape[1], partition_tokens)
+        self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+
+    def run(self, i, ev=None):
+        """Copies (if any), write, decode on pool copy i; ev = 4 events or None."""
+        kc, vc = self.pools[i % len(self.pools)]
+        if ev:
+            ev[0].record()
+        if self.pairs is not None:
+            self.ops.pkv_block_copy(kc, vc, self.pairs)
+        if ev:
+            ev[1].record()
+        self.ops.pkv_kv_write(self.k_new, self.v_new, self.slots, kc, vc)
+        if ev:
+            ev[2].record()
+        self.ops.pkv_attention_decode(self.out, self.q, kc, vc, self.bt, self.sl, self.scale,
+                                      self.part, self.ws)
+        if ev:
+            ev[3].record()
 
 
-def measured_traffic():
-    """HBM bytes per decode call from the committed counter summary, or None.
+def decode_step_state(torch, ops, w, npools, partition_tokens):
+    """Pools holding the prefill of decode workload `w`, and its step."""
+    from paged_kv_cache_330_amd.workloads import empty_device_caches, torch_tensor
+    dev = "cuda"
+    kt, vt = torch_tensor(w.k_tokens, w.dtype, dev), torch_tensor(w.v_tokens, w.dtype, dev)
+    pre = torch.from_numpy(w.prefill_rows).to(dev)
+    pre_slots = torch.from_numpy(w.prefill_slots).to(dev)
+    k_pre, v_pre = kt[pre].contiguous(), vt[pre].contiguous()
+    step = torch.from_numpy(w.step_rows).to(dev)
+    k_new, v_new = kt[step].contiguous(), vt[step].contiguous()
+    del kt, vt
+    pools = []
+    for _ in range(npools):
+        kc, vc = empty_device_caches(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim,
+                                     w.dtype, dev, fill="zero")
+        ops.pkv_kv_write(k_pre, v_pre, pre_slots, kc, vc)
+        pools.append((kc, vc))
+    del k_pre, v_pre
+    return Step(torch, ops, pools, torch_tensor(w.q, w.dtype, dev),
+                torch.from_numpy(w.block_tables).to(dev), torch.from_numpy(w.seq_lens).to(dev),
+                k_new, v_new, torch.from_numpy(w.step_slots).to(dev), None, float(w.scale),
+                partition_tokens)
 
-    The summary records the sha256 of the library sources it was taken with;
-    when the sources have changed since, the figure no longer describes the
-    kernels and None is returned.
-    """
-    import re
-    from paged_kv_cache_330_amd.build import source_digest
-    try:
-        text = open(COUNTERS).read()
-    except OSError:
-        return None
-    sha = re.search(r"kernel_sources_sha256:\s*([0-9a-f]{64})", text)
-    val = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
-    if not sha or not val or sha.group(1) != source_digest():
-        return None
-    return int(val.group(1))
+
+def sharing_step_state(torch, ops, ws, final, partition_tokens):
+    """Pool of the prefix-sharing workload at its first divergent step (with its
+    copy-on-write copies) or at its last step; returns (Step, seq_lens)."""
+    from paged_kv_cache_330_amd.workloads import empty_device_caches, torch_tensor
+    dev = "cuda"
+    kc, vc = empty_device_caches(ws.num_blocks, ws.block_size, ws.num_kv_heads, ws.head_dim,
+                                 "bf16", dev, fill="zero")
+    pk, pv, ps = ws.prefill()
+    ops.pkv_kv_write(torch_tensor(pk, "bf16", dev), torch_tensor(pv, "bf16", dev),
+                     torch.from_numpy(ps).to(dev), kc, vc)
+    st = ws.next_step()
+    while final and ws.steps_done < ws.tail_len:  # apply every step but the last
+        if len(st.copy_pairs):
+            ops.pkv_block_copy(kc, vc, torch.from_numpy(st.copy_pairs).to(dev))
+        ops.pkv_kv_write(torch_tensor(st.k_new, "bf16", dev), torch_tensor(st.v_new, "bf16", dev),
+                         torch.from_numpy(st.slot_mapping).to(dev), kc, vc)
+        st = ws.next_step()
+    pairs = torch.from_numpy(st.copy_pairs).to(dev) if len(st.copy_pairs) else None
+    step = Step(torch, ops, [(kc, vc)], torch_tensor(st.q, "bf16", dev),
+                torch.from_numpy(st.block_tables).to(dev), torch.from_numpy(st.seq_lens).to(dev),
+                torch_tensor(st.k_new, "bf16", dev), torch_tensor(st.v_new, "bf16", dev),
+                torch.from_numpy(st.slot_mapping).to(dev), pairs, float(ws.scale),
+                partition_tokens)
+    return step, st.seq_lens
+
+
+def time_steps(torch, step, steps, warmup):
+    """Warm up, then time exactly `steps` steps between two synchronisations.
+
+    Re-running a step is idempotent: its copies, writes and decode see the same
+    pool contents every time."""
+    for i in range(warmup):
+        step.run(i)
+    torch.cuda.synchronize()
+    step.ops.pkv_check_device_errors()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step.run(warmup + i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step.ops.pkv_check_device_errors()
+    ms = lambda a, b: [e[a].elapsed_time(e[b]) for e in events]  # noqa: E731
+    return wall, ms(0, 1), ms(1, 2), ms(2, 3)
+
+
+def attn_bytes(seq_lens, B, Hq, Hkv, D, bs, es):
+    """Algorithmic bytes of one decode call: K/V rows, q, fp32 out, table entries, lengths."""
+    kv = int(sum(int(L) for L in seq_lens)) * Hkv * D * 2 * es
+    entries = int(sum(math.ceil(int(L) / bs) for L in seq_lens))
+    return kv, kv + B * Hq * D * es + B * Hq * D * 4 + 4 * entries + 4 * B
+
+
+def _pct(xs, p):
+    import numpy as np
+    return float(np.percentile(xs, p))
+
+
+def summary(name, extra, seq_lens, B, Hq, Hkv, D, bs, steps, wall, t_copy, t_write, t_attn,
+            n_pairs=0, es=2):
+    """Figures of one timed workload (`es` bytes per stored element)."""
+    kv, alg = attn_bytes(seq_lens, B, Hq, Hkv, D, bs, es)
+    attn_ms = statistics.median(t_attn)
+    ms_per_step = wall * 1e3 / steps
+    row = Hkv * D * es
+    res = {
+        "workload": name, **extra, "num_seqs": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
+        "head_dim": D, "block_size": bs, "seq_len_sum": int(sum(int(L) for L in seq_lens)),
+        "ms_per_step": round(ms_per_step, 4),
+        "t_attn_us": {"median": round(attn_ms * 1e3, 2),
+                      "p10": round(_pct(t_attn, 10) * 1e3, 2),
+                      "p90": round(_pct(t_attn, 90) * 1e3, 2)},
+        "attn_kv_gbps": round(kv / (attn_ms * 1e-3) / 1e9, 2),
+        "attn_hbm_frac": round(kv / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "attn_alg_gbps": round(alg / (statistics.mean(t_attn) * 1e-3) / 1e9, 2),
+        "tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
+        "attn_tokens_per_s": round(B / (attn_ms * 1e-3), 1),
+        "t_write_us": round(statistics.median(t_write) * 1e3, 2),
+        "write_gbps": round((2 * 2 * B * row + 8 * B) / (statistics.median(t_write) * 1e-3) / 1e9, 2),
+    }
+    if n_pairs:
+        cb = 2 * 2 * n_pairs * bs * row + 16 * n_pairs
+        res["t_copy_us"] = round(statistics.median(t_copy) * 1e3, 2)
+        res["copy_pairs"] = n_pairs
+        res["copy_gbps"] = round(cb / (statistics.median(t_copy) * 1e-3) / 1e9, 2)
+    return res, kv, alg
+
+
+def report_all(torch, ops, args):
+    """One JSON line per workload other than the metric's (shorter runs)."""
+    from paged_kv_cache_330_amd.workloads import PrefixSharingWorkload, make_decode_workload
+    steps, warmup = 20, 3
+    for config, bs in ((2, None), (4, 32), (4, 64)):
+        w = make_decode_workload(config, block_size=bs)
+        st = decode_step_state(torch, ops, w, args.pools, args.partition_tokens)
+        wall, t_copy, t_write, t_attn = time_steps(torch, st, steps, warmup)
+        res, _, _ = summary(w.name, {"seed": w.seed}, w.seq_lens, w.num_seqs, w.num_q_heads,
+                            w.num_kv_heads, w.head_dim, w.block_size, steps, wall, t_copy,
+                            t_write, t_attn)
+        print(json.dumps({"report": res}), flush=True)
+        del st
+        torch.cuda.empty_cache()
+    for bs in (8, 16):
+        for final in (False, True):
+            ws = PrefixSharingWorkload(prefix_len=args.prefix, block_size=bs)
+            st, lens = sharing_step_state(torch, ops, ws, final, args.partition_tokens)
+            wall, t_copy, t_write, t_attn = time_steps(torch, st, steps, warmup)
+            n_pairs = 0 if st.pairs is None else int(st.pairs.shape[0])
+            res, kv, _ = summary(
+                "prefix_sharing", {"prefix": args.prefix, "step": ws.steps_done, "seed": ws.seed},
+                lens, ws.num_seqs, ws.num_q_heads, ws.num_kv_heads, ws.head_dim, bs, steps, wall,
+                t_copy, t_write, t_attn, n_pairs)
+            # K/V bytes held once: the prompts' prefixes and every sample's own tail
+            unique = (ws.prompts * ws.prefix_len + ws.num_seqs * (int(lens[0]) - ws.prefix_len)) \
+                * ws.num_kv_heads * ws.head_dim * 2 * 2
+            res["unique_kv_bytes"] = unique
+            res["unique_kv_gbps"] = round(unique / (res["t_attn_us"]["median"] * 1e-6) / 1e9, 2)
+            res["note"] = ("attn_kv_gbps counts the bytes every sequence reads (logical); the "
+                           "shared blocks are cache-resident, so % of HBM is not meaningful here")
+            print(json.dumps({"report": res}), flush=True)
+            del st
+            torch.cuda.empty_cache()
 
 
 def main():
@@ -155,90 +376,33 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the paged decode path "
               "here is a single-GPU build", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
 
     if args.copy_probe:
         copy_probe(torch)
         return
+    if args.read_probe:
+        read_probe(torch)
+        return
 
     from paged_kv_cache_330_amd import ops
-    from paged_kv_cache_330_amd.workloads import (empty_device_caches, make_decode_workload,
-                                                  torch_tensor)
+    from paged_kv_cache_330_amd.workloads import make_decode_workload
 
     ops.load_library()
-    dev = "cuda"
+    if args.report_all:
+        report_all(torch, ops, args)
     t_gen = time.perf_counter()
     w = make_decode_workload(args.config, block_size=args.block_size)
     t_gen = time.perf_counter() - t_gen
+    st = decode_step_state(torch, ops, w, args.pools, args.partition_tokens)
+    wall, t_copy, t_write, t_attn = time_steps(torch, st, args.steps, args.warmup)
     B, Hq, Hkv, D, bs = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
-    es = w.elem_bytes
-
-    kt, vt = torch_tensor(w.k_tokens, w.dtype, dev), torch_tensor(w.v_tokens, w.dtype, dev)
-    pre = torch.from_numpy(w.prefill_rows).to(dev)
-    pre_slots = torch.from_numpy(w.prefill_slots).to(dev)
-    k_pre, v_pre = kt[pre].contiguous(), vt[pre].contiguous()
-    step = torch.from_numpy(w.step_rows).to(dev)
-    k_new, v_new = kt[step].contiguous(), vt[step].contiguous()
-    step_slots = torch.from_numpy(w.step_slots).to(dev)
-    del kt, vt
-    pools = []
-    for _ in range(args.pools):
-        kc, vc = empty_device_caches(w.num_blocks, bs, Hkv, D, w.dtype, dev, fill="zero")
-        ops.pkv_kv_write(k_pre, v_pre, pre_slots, kc, vc)
-        pools.append((kc, vc))
-    del k_pre, v_pre
-    q = torch_tensor(w.q, w.dtype, dev)
-    bt = torch.from_numpy(w.block_tables).to(dev)
-    sl = torch.from_numpy(w.seq_lens).to(dev)
-    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
-    ws_bytes = ops.pkv_attention_workspace_bytes(pools[0][0], pools[0][1], B, Hq, bt.shape[1],
-                                                 args.partition_tokens)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    ops.pkv_check_device_errors()
-
-    def one_step(i, ev=None):
-        kc, vc = pools[i % len(pools)]
-        if ev:
-            ev[0].record()
-        ops.pkv_kv_write(k_new, v_new, step_slots, kc, vc)
-        if ev:
-            ev[1].record()
-        ops.pkv_attention_decode(out, q, kc, vc, bt, sl, float(w.scale), args.partition_tokens, ws)
-        if ev:
-            ev[2].record()
-
-    for i in range(args.warmup):
-        one_step(i)
-    torch.cuda.synchronize()
-    ops.pkv_check_device_errors()
-
-    # Timed region: exactly K steps, synchronised on both sides.
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        one_step(args.warmup + i, events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ops.pkv_check_device_errors()
-
-    t_write = [e[0].elapsed_time(e[1]) for e in events]    # ms
-    t_attn = [e[1].elapsed_time(e[2]) for e in events]
+    rep, kv_bytes, alg = summary(w.name, {}, w.seq_lens, B, Hq, Hkv, D, bs, args.steps, wall,
+                                 t_copy, t_write, t_attn, es=w.elem_bytes)
     ms_per_step = wall * 1e3 / args.steps
-    attn_ms = statistics.median(t_attn)
-    write_ms = statistics.median(t_write)
-
-    total_tokens = int(w.seq_lens.sum())
-    kv_bytes = w.kv_bytes()
-    table_entries = int(sum(math.ceil(int(L) / bs) for L in w.seq_lens))
-    attn_alg_bytes = kv_bytes + B * Hq * D * es + B * Hq * D * 4 + 4 * table_entries + 4 * B
-    write_alg_bytes = 2 * (2 * B * Hkv * D * es) + 8 * B
-    flops = 4 * Hq * D * total_tokens
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    attn_gbps = kv_bytes / (attn_ms * 1e-3) / 1e9
-    achieved = attn_alg_bytes / (statistics.mean(t_attn) * 1e-3) / 1e9
-
+    achieved = alg / (statistics.mean(t_attn) * 1e-3) / 1e9
+    flops = 4 * Hq * D * int(w.seq_lens.sum())
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -254,24 +418,22 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": w.name, "num_seqs": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
-            "head_dim": D, "block_size": bs, "seq_len_sum": total_tokens,
+            "head_dim": D, "block_size": bs, "seq_len_sum": rep["seq_len_sum"],
             "seq_len_max": int(w.seq_lens.max()), "seq_len_min": int(w.seq_lens.min()),
             "schedule": ("balanced" if args.partition_tokens == 0 else
                          f"partitions of {args.partition_tokens} tokens"),
-            "num_blocks": w.num_blocks,
-            "kv_pool_copies": len(pools), "seed": w.seed, "out_dtype": "f32",
+            "num_blocks": w.num_blocks, "kv_pool_copies": len(st.pools), "seed": w.seed,
+            "out_dtype": "f32",
         },
         "hbm_frac_step": round(value / HBM_PEAK_GBPS, 4),
-        "attn_kv_gbps": round(attn_gbps, 2),
-        "attn_hbm_frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
-        "tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
-        "attn_tokens_per_s": round(B / (attn_ms * 1e-3), 1),
-        "t_attn_us": {"median": round(attn_ms * 1e3, 2),
-                      "p10": round(float(np.percentile(t_attn, 10)) * 1e3, 2),
-                      "p90": round(float(np.percentile(t_attn, 90)) * 1e3, 2)},
-        "t_write_us": round(write_ms * 1e3, 2),
-        "write_gbps": round(write_alg_bytes / (write_ms * 1e-3) / 1e9, 2),
-        "attn_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 3),
+        "attn_kv_gbps": rep["attn_kv_gbps"],
+        "attn_hbm_frac": rep["attn_hbm_frac"],
+        "tokens_per_s": rep["tokens_per_s"],
+        "attn_tokens_per_s": rep["attn_tokens_per_s"],
+        "t_attn_us": rep["t_attn_us"],
+        "t_write_us": rep["t_write_us"],
+        "write_gbps": rep["write_gbps"],
+        "attn_tflops": round(flops / (statistics.median(t_attn) * 1e-3) / 1e12, 3),
         "kv_bytes_per_step": kv_bytes,
         "roofline": {
             "kernel": ("pkv_attention_decode: " + ("decode_balanced_kernel + balanced_reduce_kernel"
@@ -283,10 +445,11 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": (measured_traffic() if (args.config, args.block_size,
                                                  args.partition_tokens) == (3, None, 0) else None),
-            "algorithmic_bytes_per_launch": attn_alg_bytes,
+            "algorithmic_bytes_per_launch": alg,
         },
         "workload_gen_s": round(t_gen, 2),
     }
+    del st
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
         res["gpu_over_cpu"] = round(res["attn_kv_gbps"] / res["cpu_baseline"]["value"], 1)

@@ -18,6 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
+PROBE_LIB = os.path.join(PKG, "libpkv_probe.so")  # measurement support for bench.py
 SOURCES = ["api.hip", "kv_write.hip", "block_copy.hip", "attention_mfma.hip", "attention_valu.hip"]
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
@@ -30,8 +31,8 @@ def source_digest() -> str:
     """
     import glob
     import hashlib
-    files = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h")) +
-                   [os.path.join(ROOT, "include", "pagedkv.h")])
+    files = sorted(f for f in glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h"))
+                   if not f.endswith("stream_probe.hip")) + [os.path.join(ROOT, "include", "pagedkv.h")]
     h = hashlib.sha256()
     for f in sorted(files, key=lambda f: os.path.relpath(f, ROOT)):
         h.update(os.path.basename(f).encode())
@@ -79,6 +80,10 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp"
+    _run([hipcc(), *compile_flags(), "-shared", os.path.join(CSRC, "stream_probe.hip"), "-o", tmp],
+         verbose)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

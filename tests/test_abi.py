@@ -8,6 +8,7 @@ a machine without a GPU.
 import ctypes
 import os
 import subprocess
+import sys
 
 import pytest
 
@@ -154,3 +155,38 @@ def test_workspace_size_balanced_schedule(lib):
     assert ws_bytes(lib, desc(), 2048, 32, 64, 0) == got
     # beyond 2048 sequences the partition grid takes over
     assert ws_bytes(lib, desc(), 4096, 32, 64, 0) == 2 * (4096 * 32 * 2 * 4) + 4096 * 32 * 2 * 128 * 4
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    # No fallback: with the library absent the binding raises instead of
+    # computing anything some other way.
+    code = (
+        "import os, sys\n"
+        f"sys.path.insert(0, {os.path.dirname(os.path.dirname(os.path.abspath(__file__)))!r})\n"
+        "os.environ['PKV_LIBRARY'] = os.path.join(sys.argv[1], 'absent.so')\n"
+        "from paged_kv_cache_330_amd import ops\n"
+        "try:\n"
+        "    ops.load_library()\n"
+        "except RuntimeError as e:\n"
+        "    print('raised:', e)\n"
+        "    sys.exit(0)\n"
+        "sys.exit(1)\n")
+    r = subprocess.run([sys.executable, "-c", code, str(tmp_path)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "no fallback" in r.stdout
+
+
+def test_product_package_does_not_use_the_oracle():
+    pkg = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                       "paged_kv_cache_330_amd")
+    for root, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(root, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+    code = ("import sys\n"
+            f"sys.path.insert(0, {os.path.dirname(pkg)!r})\n"
+            "import paged_kv_cache_330_amd, paged_kv_cache_330_amd.ops, paged_kv_cache_330_amd.workloads\n"
+            "print('oracle' in sys.modules)\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True)
+    assert r.stdout.strip() == "False"

@@ -365,3 +365,20 @@ def test_prefix_sharing_copy_on_write(ops, prefix, bs):
                 k_log, _ = ws.logical_tokens(b, int(st.seq_lens[b]))
                 assert np.array_equal(oracle.gather_sequence(rk, st.block_tables[b], len(k_log)), k_log)
     assert n_copies == (28 if prefix % bs else 0)
+
+
+def test_workspace_reused_across_calls(ops):
+    # One workspace for consecutive calls of different batches and schedules:
+    # nothing from an earlier call may leak into a later one.
+    w1 = workload(3, (900, 5000, 40, 17), 16)
+    w2 = workload(3, (3000, 1, 700), 16)
+    ws = torch.empty(1 << 26, dtype=torch.uint8, device="cuda")
+    for w in (w1, w2, w1):
+        kc, vc, _ = gpu_step(ops, w, decode=False)
+        out = torch.empty(w.q.shape, dtype=torch.float32, device="cuda")
+        ops.pkv_attention_decode(out, torch_tensor(w.q, "bf16", "cuda"), kc, vc,
+                                 torch.from_numpy(w.block_tables).cuda(),
+                                 torch.from_numpy(w.seq_lens).cuda(), float(w.scale), 0, ws)
+        ops.pkv_check_device_errors()
+        rk, rv = oracle_caches(w)
+        assert_close(out.cpu().numpy(), oracle_decode(w, rk, rv), TOL["bf16"], f"batch {w.num_seqs}")
