@@ -59,6 +59,10 @@ def parse():
                    help="only time a plain streaming read of 4 GiB (context for the roofline)")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device copy (HBM counter calibration)")
+    p.add_argument("--counter-pass", action="store_true",
+                   help="only run 4 decode calls of the workload (a 1 GiB write between calls "
+                        "evicts the pool from the caches), then 3 streaming reads of 2 GiB: "
+                        "a short program for hardware-counter passes")
     return p.parse_args()
 
 
@@ -100,6 +104,36 @@ def read_probe(torch):
     print(json.dumps({"read_probe_bytes": buf.numel(), "gbps_by_workgroups": res,
                       "best_gbps": max(res.values()),
                       "best_frac_of_peak": round(max(res.values()) / HBM_PEAK_GBPS, 4)}), flush=True)
+
+
+def counter_pass(torch, args):
+    """Four decode calls and three plain streaming reads, nothing else timed."""
+    import ctypes
+    from paged_kv_cache_330_amd import ops
+    from paged_kv_cache_330_amd.build import PROBE_LIB
+    from paged_kv_cache_330_amd.workloads import make_decode_workload
+    ops.load_library()
+    w = make_decode_workload(args.config, block_size=args.block_size)
+    st = decode_step_state(torch, ops, w, 1, args.partition_tokens)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    for i in range(4):
+        flush.fill_(i)
+        st.run(0)
+    torch.cuda.synchronize()
+    ops.pkv_check_device_errors()
+    del st, flush
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.pkv_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                          ctypes.c_int, ctypes.c_void_p]
+    buf = torch.ones(2 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for _ in range(3):
+        if lib.pkv_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), buf.numel(),
+                                     ctypes.c_void_p(sink.data_ptr()), 65536, stream) != 0:
+            raise RuntimeError("stream probe launch failed")
+    torch.cuda.synchronize()
+    print(json.dumps({"counter_pass": "done", "workload": w.name}), flush=True)
 
 
 def measured_traffic():
@@ -383,6 +417,9 @@ def main():
         return
     if args.read_probe:
         read_probe(torch)
+        return
+    if args.counter_pass:
+        counter_pass(torch, args)
         return
 
     from paged_kv_cache_330_amd import ops

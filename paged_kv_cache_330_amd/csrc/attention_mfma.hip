@@ -67,11 +67,19 @@ struct KVTile {
   u32x4_t v[TC][4];
 };
 
+// With PKV_K_VIA_LDS the K rows are loaded like the V rows (each load
+// instruction covers 4 whole 256-byte rows instead of 64 bytes of 16 rows)
+// and put into the MFMA operand layout through a wave-private LDS tile of
+// 16 rows, each padded to 17 x 16 bytes so that both the row writes and the
+// column reads are free of bank conflicts.
+constexpr int kKRowPad = 17;  // 16-byte units per LDS row
+
 struct TileCtx {
-  const uint16_t* kbase;  // K pool + kv head offset + this lane's d-chunk
+  const uint16_t* kbase;  // K pool + kv head offset + this lane's d-chunk (or dims)
   const uint16_t* vbase;  // V pool + kv head offset + this lane's dims
-  const uint16_t* kdead;  // this wave's query row + this lane's d-chunk (see load_tile)
+  const uint16_t* kdead;  // this wave's query row + this lane's offset (see load_tile)
   const uint16_t* vdead;  // this wave's query row + this lane's dims
+  u32x4_t* k_lds;         // this wave's K transpose tile (PKV_K_VIA_LDS)
   int64_t tok_stride;     // elements between consecutive slots
   const int* s_bt;        // physical block ids of the window (LDS)
   int blk0;               // logical block of s_bt[0]
@@ -114,6 +122,16 @@ __device__ __forceinline__ void load_tile(KVTile<TC>& r, int t0, const TileCtx& 
 #pragma unroll
       for (int i = 0; i < 4; ++i) pv[i] = c.s_bt[min(tce + 4 * c.qr + i, c.end - 1) / BS - c.blk0];
     }
+#if PKV_K_VIA_LDS
+    (void)pk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // row 4 qr + i, dims 8 col .. 8 col + 7
+      const int tv = min(tce + 4 * c.qr + i, c.end - 1);
+      const int64_t row = ((int64_t)pv[i] * BS + (tv & (BS - 1))) * c.tok_stride;
+      r.k[ch][i] = load_kv(dead ? c.kdead : c.kbase + row);
+      r.v[ch][i] = load_kv(dead ? c.vdead : c.vbase + row);
+    }
+#else
     const uint16_t* kp =
         dead ? c.kdead : c.kbase + ((int64_t)pk * BS + (tk & (BS - 1))) * c.tok_stride;
 #pragma unroll
@@ -125,6 +143,7 @@ __device__ __forceinline__ void load_tile(KVTile<TC>& r, int t0, const TileCtx& 
           dead ? c.vdead : c.vbase + ((int64_t)pv[i] * BS + (tv & (BS - 1))) * c.tok_stride;
       r.v[ch][i] = load_kv(vp);
     }
+#endif
   }
 }
 
@@ -147,15 +166,27 @@ struct WaveState {
 template <int G, int TC>
 __device__ __forceinline__ void compute_tile(const KVTile<TC>& r, int t0, int end,
                                              const bf16x8_t (&qop)[4], float scale_log2e,
-                                             int qr, WaveState<G>& st) {
+                                             const TileCtx& ctx, WaveState<G>& st) {
+  const int qr = ctx.qr;
   float x[TC][4];
   float mt = -INFINITY;
 #pragma unroll
   for (int c = 0; c < TC; ++c) {
+    u32x4_t kop[4];
+#if PKV_K_VIA_LDS
+    // rows as loaded -> LDS -> lane (col, qr) takes d-chunk 4 s + qr of row col
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ctx.k_lds[(4 * qr + i) * kKRowPad + ctx.col] = r.k[c][i];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) kop[s] = ctx.k_lds[ctx.col * kKRowPad + 4 * s + qr];
+#else
+#pragma unroll
+    for (int s = 0; s < 4; ++s) kop[s] = r.k[c][s];
+#endif
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[c][s]),
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop[s]),
                                                       qop[s], sacc, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -242,7 +273,7 @@ __device__ __forceinline__ void stream_window(const DecodeArgs& a, const TileCtx
   while (true) {
     KVTile<TC> nxt;
     load_tile<BS, TC>(nxt, t0 + PKV_PREFETCH_TILES * TILE, c);
-    compute_tile<G, TC>(cur, t0, c.end, qop, a.scale_log2e, c.qr, st);
+    compute_tile<G, TC>(cur, t0, c.end, qop, a.scale_log2e, c, st);
     t0 += TILE;
     if (t0 >= c.end) break;
 #if PKV_PREFETCH_TILES >= 2
@@ -259,9 +290,9 @@ __device__ __forceinline__ void stream_window(const DecodeArgs& a, const TileCtx
 // of up to kMaxPartitionTokens tokens go to LDS once for all waves.  Every
 // thread of the workgroup calls this with the same range.
 template <int G, int BS, int TC>
-__device__ __forceinline__ void attend_range(const DecodeArgs& a, int* s_bt, int b, int kvh,
-                                             int begin, int end, const bf16x8_t (&qop)[4],
-                                             WaveState<G>& st) {
+__device__ __forceinline__ void attend_range(const DecodeArgs& a, int* s_bt, u32x4_t* k_lds, int b,
+                                             int kvh, int begin, int end,
+                                             const bf16x8_t (&qop)[4], WaveState<G>& st) {
   const int lane = threadIdx.x & 63;
   const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
   const uint16_t* qrow =
@@ -270,9 +301,16 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, int* s_bt, int
   c.tok_stride = (int64_t)a.num_kv_heads * kD;
   c.col = lane & 15;
   c.qr = lane >> 4;
+#if PKV_K_VIA_LDS
+  c.kbase = static_cast<const uint16_t*>(a.k_cache) + (int64_t)kvh * kD + 8 * c.col;
+  c.kdead = qrow + 8 * c.col;
+  c.k_lds = k_lds;
+#else
   c.kbase = static_cast<const uint16_t*>(a.k_cache) + (int64_t)kvh * kD + 8 * c.qr;
-  c.vbase = static_cast<const uint16_t*>(a.v_cache) + (int64_t)kvh * kD + 8 * c.col;
   c.kdead = qrow + 8 * c.qr;  // + 32 s: 16 bytes inside the 128-element row
+  c.k_lds = nullptr;
+#endif
+  c.vbase = static_cast<const uint16_t*>(a.v_cache) + (int64_t)kvh * kD + 8 * c.col;
   c.vdead = qrow + 8 * c.col;
   c.s_bt = s_bt;
   for (int w0 = begin; w0 < end; w0 += kMaxPartitionTokens) {
@@ -363,6 +401,7 @@ template <int G, int BS, int TC>
 __global__ __launch_bounds__(kMaxWaves * 64) void decode_mfma_kernel(DecodeArgs a) {
   static_assert(16 % G == 0, "group must divide 16");
   __shared__ int s_bt[kMaxPartitionTokens / BS + 1];
+  __shared__ u32x4_t s_kt[PKV_K_VIA_LDS ? kMaxWaves * 16 * kKRowPad : 1];
   const int kh = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kvh = blockIdx.x * kh + wave;
@@ -378,7 +417,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mfma_kernel(DecodeArgs 
   load_query<G>(a, b, kvh, lane & 15, lane >> 4, qop);
   WaveState<G> st;
   st.reset();
-  attend_range<G, BS, TC>(a, s_bt, b, kvh, pt.begin, pt.end, qop, st);
+  attend_range<G, BS, TC>(a, s_bt, s_kt + wave * 16 * kKRowPad, b, kvh, pt.begin, pt.end, qop,
+                          st);
   Sink sink{nullptr, nullptr, nullptr, 0, 0};
   if (pt.count > 1) {
     sink = Sink{a.ws_acc, a.ws_max, a.ws_sum,
@@ -411,6 +451,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) PKV_BALANCED_OCCUPANCY void decode_
     DecodeArgs a) {
   static_assert(16 % G == 0, "group must divide 16");
   __shared__ int s_bt[kMaxPartitionTokens / BS + 1];
+  __shared__ u32x4_t s_kt[PKV_K_VIA_LDS ? kMaxWaves * 16 * kKRowPad : 1];
   __shared__ int s_cc[kMaxBalancedSeqs + 1];
   __shared__ int s_wsum[kMaxWaves];
 
@@ -483,7 +524,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) PKV_BALANCED_OCCUPANCY void decode_
     load_query<G>(a, b, kvh, lane & 15, lane >> 4, qop);
     WaveState<G> st;
     st.reset();
-    attend_range<G, BS, TC>(a, s_bt, b, kvh, tok_begin, tok_end, qop, st);
+    attend_range<G, BS, TC>(a, s_bt, s_kt + wave * 16 * kKRowPad, b, kvh, tok_begin, tok_end,
+                            qop, st);
     Sink sink{nullptr, nullptr, nullptr, 0, 0};
     if (!(first && last))
       sink = Sink{a.ws_acc, a.ws_max, a.ws_sum,
