@@ -22,20 +22,27 @@
 // once for all waves.
 //
 // Inside a wave (lane = 16 * qr + col), per 16-token chunk:
-//   Q.K^T  v_mfma_f32_16x16x32_bf16 with the K rows as the A operand straight
-//          from HBM (lane holds 8 bf16 of token `col`, d-chunk 4 s + qr in
-//          k-step s: each load instruction reads 64 contiguous bytes of 16
-//          rows) and the query group as the B operand (column col = query
-//          head col % G, replicated).  Result lane (col, qr), register i =
-//          score of head col % G with token 4 qr + i.
+//   Q.K^T  v_mfma_f32_16x16x32_bf16 with the K rows as the A operand (lane
+//          holds 8 bf16 of token `col`, d-chunk 4 s + qr in k-step s) and the
+//          query group as the B operand (column col = query head col % G,
+//          replicated).  Result lane (col, qr), register i = score of head
+//          col % G with token 4 qr + i.
 //   softmax exp2 on the hardware unit, running max over the chunk(s) of a
 //          tile with two cross-row shuffles.
-//   P.V    on the vector ALUs in fp32 (p is never rounded to bf16): lane owns
-//          output dims 8 col .. 8 col + 7 and tokens 4 qr + i (each V load
-//          instruction reads 4 whole 256-byte rows); accumulator slot R holds
-//          query head gsel[R], the head of the lane that DPP row rotation R
-//          reaches, so that head's probabilities and rescale factors arrive by
-//          the same rotation.
+//   P.V    for G >= 2 on the matrix cores (v_mfma_f32_16x16x16_bf16, fp32
+//          accumulate): out^T = V^T P, B = P straight from the score registers
+//          (lane (col, qr) holds head col % G, tokens 4 qr + i), split into a
+//          bf16 high part and a bf16 remainder so that p keeps 16 significant
+//          bits, never a single bf16 rounding; A = V^T read column-wise from the
+//          V rows in LDS.  For G = 1 (15 of 16 MFMA columns would repeat the
+//          head) on the vector ALUs in fp32: lane owns output dims
+//          8 col .. 8 col + 7 and tokens 4 qr + i; accumulator slot R holds query
+//          head gsel[R], the head of the lane that DPP row rotation R reaches,
+//          so that head's probabilities and rescale factors arrive by the same
+//          rotation.
+//   loads  every K/V load instruction reads 4 whole 256-byte rows (lane
+//          (col, qr): 16 bytes of rows 4 qr + i); K reaches the A-operand
+//          layout of Q.K^T through a padded wave-private LDS tile.
 //
 // Two schedules:
 //  * decode_mfma_kernel, partition grid: workgroup (kv-head group, sequence,
@@ -80,6 +87,7 @@ struct TileCtx {
   const uint16_t* kdead;  // this wave's query row + this lane's offset (see load_tile)
   const uint16_t* vdead;  // this wave's query row + this lane's dims
   u32x4_t* k_lds;         // this wave's K transpose tile (PKV_K_VIA_LDS)
+  u32x4_t* v_lds;         // this wave's V tile, read column-wise (P.V on the matrix cores)
   int64_t tok_stride;     // elements between consecutive slots
   const int* s_bt;        // physical block ids of the window (LDS)
   int blk0;               // logical block of s_bt[0]
@@ -147,9 +155,30 @@ __device__ __forceinline__ void load_tile(KVTile<TC>& r, int t0, const TileCtx& 
   }
 }
 
-// Running softmax state of one wave for the G heads of its kv head.
+// P.V runs on the matrix cores for query groups of at least
+// PKV_PV_MFMA_MIN_GROUP heads; a single head would use one MFMA column in 16,
+// so it stays on the vector ALUs.
 template <int G>
-struct WaveState {
+constexpr bool kPvOnMfma = G >= PKV_PV_MFMA_MIN_GROUP;
+
+// Running softmax state of one wave for the G heads of its kv head.
+template <int G, bool kMfma = kPvOnMfma<G>>
+struct WaveState;
+
+template <int G>
+struct WaveState<G, true> {
+  float m, l;   // max and (this lane's tokens') sum of head col % G
+  f32x4_t o[8]; // tile j, register i: output of head col % G, dim 16 j + 4 qr + i
+  __device__ __forceinline__ void reset() {
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+};
+
+template <int G>
+struct WaveState<G, false> {
   float m, l;        // max and sum of head col % G (copies in every column with that head)
   float acc[G][8];   // slot R: head gsel[R], dims 8 col .. 8 col + 7, this lane's token rows
   __device__ __forceinline__ void reset() {
@@ -209,25 +238,64 @@ __device__ __forceinline__ void compute_tile(const KVTile<TC>& r, int t0, int en
       psum += x[c][i];
     }
   st.l = st.l * alpha + psum;
-  static_for<G>([&](auto rr) {
-    constexpr int R = decltype(rr)::value;
-    const float ar = row_ror<R>(alpha);
+  if constexpr (kPvOnMfma<G>) {
+    // P.V on the matrix cores: out^T[d][h] += sum_t V[t][d] P[t][h] with
+    // v_mfma_f32_16x16x16_bf16, 16 dims per tile.  B = P: lane (col, qr) already
+    // holds P[4 qr + i][head col % G].  p is split into bf16 hi + lo (the top 8
+    // and the next 8 mantissa bits), two products each, so p keeps 16 bits.
+    // A = V^T: lane (col, qr) takes V[4 qr + i][16 j + col], read column-wise
+    // from the V rows this wave wrote to LDS.
 #pragma unroll
-    for (int e = 0; e < 8; ++e) st.acc[R][e] *= ar;
-  });
+    for (int j = 0; j < 8; ++j) st.o[j] *= alpha;
+    const uint16_t* vcol = reinterpret_cast<const uint16_t*>(ctx.v_lds);
 #pragma unroll
-  for (int c = 0; c < TC; ++c)
+    for (int c = 0; c < TC; ++c) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float vf[8];
-      unpack_bf16x8(r.v[c][i], vf);
-      static_for<G>([&](auto rr) {
-        constexpr int R = decltype(rr)::value;
-        const float pr = row_ror<R>(x[c][i]);
+      for (int i = 0; i < 4; ++i) ctx.v_lds[(4 * qr + i) * kKRowPad + ctx.col] = r.v[c][i];
+      uint32_t hb[4], lb[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) st.acc[R][e] = fmaf(pr, vf[e], st.acc[R][e]);
-      });
+      for (int i = 0; i < 4; ++i) {
+        hb[i] = __float_as_uint(x[c][i]) & 0xFFFF0000u;
+        lb[i] = __float_as_uint(x[c][i] - __uint_as_float(hb[i]));
+      }
+      const uint32_t hi[2] = {__builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u),
+                              __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u)};
+      const uint32_t lo[2] = {__builtin_amdgcn_perm(lb[1], lb[0], 0x07060302u),
+                              __builtin_amdgcn_perm(lb[3], lb[2], 0x07060302u)};
+      const bf16x4_t phi = __builtin_bit_cast(bf16x4_t, hi);
+      const bf16x4_t plo = __builtin_bit_cast(bf16x4_t, lo);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint16_t e[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) e[t] = vcol[(4 * qr + t) * (kKRowPad * 8) + 16 * j + ctx.col];
+        const uint32_t va[2] = {e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16)};
+        const bf16x4_t vt = __builtin_bit_cast(bf16x4_t, va);
+        st.o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, phi, st.o[j], 0, 0, 0);
+        st.o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, plo, st.o[j], 0, 0, 0);
+      }
     }
+  } else {
+    static_for<G>([&](auto rr) {
+      constexpr int R = decltype(rr)::value;
+      const float ar = row_ror<R>(alpha);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) st.acc[R][e] *= ar;
+    });
+#pragma unroll
+    for (int c = 0; c < TC; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float vf[8];
+        unpack_bf16x8(r.v[c][i], vf);
+        static_for<G>([&](auto rr) {
+          constexpr int R = decltype(rr)::value;
+          const float pr = row_ror<R>(x[c][i]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) st.acc[R][e] = fmaf(pr, vf[e], st.acc[R][e]);
+        });
+      }
+  }
 }
 
 // Query operand of the group of kv head kvh, sequence b.
@@ -290,8 +358,8 @@ __device__ __forceinline__ void stream_window(const DecodeArgs& a, const TileCtx
 // of up to kMaxPartitionTokens tokens go to LDS once for all waves.  Every
 // thread of the workgroup calls this with the same range.
 template <int G, int BS, int TC>
-__device__ __forceinline__ void attend_range(const DecodeArgs& a, int* s_bt, u32x4_t* k_lds, int b,
-                                             int kvh, int begin, int end,
+__device__ __forceinline__ void attend_range(const DecodeArgs& a, int* s_bt, u32x4_t* k_lds,
+                                             u32x4_t* v_lds, int b, int kvh, int begin, int end,
                                              const bf16x8_t (&qop)[4], WaveState<G>& st) {
   const int lane = threadIdx.x & 63;
   const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
@@ -312,6 +380,7 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, int* s_bt, u32
 #endif
   c.vbase = static_cast<const uint16_t*>(a.v_cache) + (int64_t)kvh * kD + 8 * c.col;
   c.vdead = qrow + 8 * c.col;
+  c.v_lds = v_lds;
   c.s_bt = s_bt;
   for (int w0 = begin; w0 < end; w0 += kMaxPartitionTokens) {
     const int wend = min(end, w0 + kMaxPartitionTokens);
@@ -337,48 +406,74 @@ struct Sink {
   int64_t stride;  // rows between consecutive heads
 };
 
-// Sums the wave's four token rows, then writes either the normalised output
-// rows of the G heads (sink.acc == nullptr) or their partial results.
+// Completes the wave's sums over its token rows, then writes either the
+// normalised output rows of the G heads (sink.acc == nullptr) or their
+// partial results.
 template <int G>
 __device__ __forceinline__ void finish_wave(const DecodeArgs& a, WaveState<G>& st, int b, int kvh,
                                             const Sink& sink) {
   const int lane = threadIdx.x & 63;
   const int col = lane & 15, qr = lane >> 4;
-#pragma unroll
-  for (int r = 0; r < G; ++r)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      st.acc[r][e] += __shfl_xor(st.acc[r][e], 16);
-      st.acc[r][e] += __shfl_xor(st.acc[r][e], 32);
-    }
-  st.l += __shfl_xor(st.l, 16);
-  st.l += __shfl_xor(st.l, 32);
-  // Head, max and sum of every slot, by the same rotation as the accumulation
-  // (computed by all lanes: DPP reads neighbouring lanes).
-  int hsel[G];
-  float msel[G], lsel[G];
-  static_for<G>([&](auto rr) {
-    constexpr int R = decltype(rr)::value;
-    hsel[R] = row_ror<R>(col % G);
-    msel[R] = row_ror<R>(st.m);
-    lsel[R] = row_ror<R>(st.l);
-  });
-  if (qr != 0) return;
-#pragma unroll
-  for (int r = 0; r < G; ++r) {
+  if constexpr (kPvOnMfma<G>) {
+    // The matrix cores already summed over the tokens; only l needs the rows.
+    st.l += __shfl_xor(st.l, 16);
+    st.l += __shfl_xor(st.l, 32);
+    if (col >= G) return;  // columns >= G repeat heads 0 .. G-1
+    const int h = col;
     if (sink.acc == nullptr) {
-      const int64_t o = ((int64_t)b * a.num_q_heads + kvh * G + hsel[r]) * kD + 8 * col;
-      const float inv = 1.f / lsel[r];
+      const int64_t o = ((int64_t)b * a.num_q_heads + kvh * G + h) * kD + 4 * qr;
+      const float inv = 1.f / st.l;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) store_out(a, o + e, st.acc[r][e] * inv);
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) store_out(a, o + 16 * j + i, st.o[j][i] * inv);
     } else {
-      const int64_t row = sink.row0 + hsel[r] * sink.stride;
-      float* dst = sink.acc + row * kD + 8 * col;
+      const int64_t row = sink.row0 + h * sink.stride;
+      float* dst = sink.acc + row * kD + 4 * qr;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dst[e] = st.acc[r][e];
-      if (col == 0) {
-        sink.max[row] = msel[r];
-        sink.sum[row] = lsel[r];
+      for (int j = 0; j < 8; ++j) *reinterpret_cast<f32x4_t*>(dst + 16 * j) = st.o[j];
+      if (qr == 0) {
+        sink.max[row] = st.m;
+        sink.sum[row] = st.l;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < G; ++r)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        st.acc[r][e] += __shfl_xor(st.acc[r][e], 16);
+        st.acc[r][e] += __shfl_xor(st.acc[r][e], 32);
+      }
+    st.l += __shfl_xor(st.l, 16);
+    st.l += __shfl_xor(st.l, 32);
+    // Head, max and sum of every slot, by the same rotation as the accumulation
+    // (computed by all lanes: DPP reads neighbouring lanes).
+    int hsel[G];
+    float msel[G], lsel[G];
+    static_for<G>([&](auto rr) {
+      constexpr int R = decltype(rr)::value;
+      hsel[R] = row_ror<R>(col % G);
+      msel[R] = row_ror<R>(st.m);
+      lsel[R] = row_ror<R>(st.l);
+    });
+    if (qr != 0) return;
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+      if (sink.acc == nullptr) {
+        const int64_t o = ((int64_t)b * a.num_q_heads + kvh * G + hsel[r]) * kD + 8 * col;
+        const float inv = 1.f / lsel[r];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) store_out(a, o + e, st.acc[r][e] * inv);
+      } else {
+        const int64_t row = sink.row0 + hsel[r] * sink.stride;
+        float* dst = sink.acc + row * kD + 8 * col;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dst[e] = st.acc[r][e];
+        if (col == 0) {
+          sink.max[row] = msel[r];
+          sink.sum[row] = lsel[r];
+        }
       }
     }
   }
@@ -402,6 +497,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mfma_kernel(DecodeArgs 
   static_assert(16 % G == 0, "group must divide 16");
   __shared__ int s_bt[kMaxPartitionTokens / BS + 1];
   __shared__ u32x4_t s_kt[PKV_K_VIA_LDS ? kMaxWaves * 16 * kKRowPad : 1];
+  __shared__ u32x4_t s_vt[kPvOnMfma<G> ? kMaxWaves * 16 * kKRowPad : 1];
   const int kh = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kvh = blockIdx.x * kh + wave;
@@ -417,8 +513,9 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mfma_kernel(DecodeArgs 
   load_query<G>(a, b, kvh, lane & 15, lane >> 4, qop);
   WaveState<G> st;
   st.reset();
-  attend_range<G, BS, TC>(a, s_bt, s_kt + wave * 16 * kKRowPad, b, kvh, pt.begin, pt.end, qop,
-                          st);
+  attend_range<G, BS, TC>(a, s_bt, s_kt + (PKV_K_VIA_LDS ? wave * 16 * kKRowPad : 0),
+                          s_vt + (kPvOnMfma<G> ? wave * 16 * kKRowPad : 0), b, kvh, pt.begin,
+                          pt.end, qop, st);
   Sink sink{nullptr, nullptr, nullptr, 0, 0};
   if (pt.count > 1) {
     sink = Sink{a.ws_acc, a.ws_max, a.ws_sum,
@@ -452,6 +549,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) PKV_BALANCED_OCCUPANCY void decode_
   static_assert(16 % G == 0, "group must divide 16");
   __shared__ int s_bt[kMaxPartitionTokens / BS + 1];
   __shared__ u32x4_t s_kt[PKV_K_VIA_LDS ? kMaxWaves * 16 * kKRowPad : 1];
+  __shared__ u32x4_t s_vt[kPvOnMfma<G> ? kMaxWaves * 16 * kKRowPad : 1];
   __shared__ int s_cc[kMaxBalancedSeqs + 1];
   __shared__ int s_wsum[kMaxWaves];
 
@@ -524,8 +622,9 @@ __global__ __launch_bounds__(kMaxWaves * 64) PKV_BALANCED_OCCUPANCY void decode_
     load_query<G>(a, b, kvh, lane & 15, lane >> 4, qop);
     WaveState<G> st;
     st.reset();
-    attend_range<G, BS, TC>(a, s_bt, s_kt + wave * 16 * kKRowPad, b, kvh, tok_begin, tok_end,
-                            qop, st);
+    attend_range<G, BS, TC>(a, s_bt, s_kt + (PKV_K_VIA_LDS ? wave * 16 * kKRowPad : 0),
+                            s_vt + (kPvOnMfma<G> ? wave * 16 * kKRowPad : 0), b, kvh, tok_begin,
+                            tok_end, qop, st);
     Sink sink{nullptr, nullptr, nullptr, 0, 0};
     if (!(first && last))
       sink = Sink{a.ws_acc, a.ws_max, a.ws_sum,

@@ -33,6 +33,9 @@ constexpr int kMaxBalancedSeqs = 2048;     // batch limit of the balanced schedu
 #ifndef PKV_K_VIA_LDS
 #define PKV_K_VIA_LDS 1         // K rows loaded 4 whole rows per instruction, transposed in LDS (0: MFMA layout loads)
 #endif
+#ifndef PKV_PV_MFMA_MIN_GROUP
+#define PKV_PV_MFMA_MIN_GROUP 2 // P.V on the matrix cores for query groups this large (p as bf16 hi + lo)
+#endif
 #ifndef PKV_BALANCED_WAVES_PER_EU
 #define PKV_BALANCED_WAVES_PER_EU 0  // > 0: ask the compiler for this occupancy (may spill)
 #endif
