@@ -368,6 +368,42 @@ def summary(name, extra, seq_lens, B, Hq, Hkv, D, bs, steps, wall, t_copy, t_wri
     return res, kv, alg
 
 
+def swap_report(torch, ops, blocks=2048, reps=5):
+    """Swap 2048 blocks of the batch-256 GQA pool shape (bs 16, 8 kv heads,
+    head_dim 128, bf16: 64 KiB of K+V per block) out to pinned host memory and
+    back in, with pkv_block_transfer; GB/s of K+V moved each way."""
+    dev = "cuda"
+    shape = (blocks * 2, 16, 8, 128)
+    kc = torch.randn(shape, device=dev).to(torch.bfloat16)
+    vc = torch.randn(shape, device=dev).to(torch.bfloat16)
+    hk = torch.empty((blocks, 16, 8, 128), dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty_like(hk, pin_memory=True)
+    src = torch.randperm(blocks * 2, device=dev)[:blocks]
+    out_pairs = torch.stack([src, torch.arange(blocks, device=dev)], 1).contiguous()
+    in_pairs = torch.stack([torch.arange(blocks, device=dev), src], 1).contiguous()
+    nbytes = 2 * blocks * 16 * 8 * 128 * 2
+    res = {"workload": "block_swap", "blocks": blocks, "bytes_each_way": nbytes}
+    for name, call in (("out", lambda: ops.pkv_block_transfer(hk, hv, kc, vc, out_pairs)),
+                       ("in", lambda: ops.pkv_block_transfer(kc, vc, hk, hv, in_pairs))):
+        call()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            call()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ops.pkv_check_device_errors()
+        ms = statistics.median(ts)
+        res[f"swap_{name}_us"] = round(ms * 1e3, 1)
+        res[f"swap_{name}_gbps"] = round(nbytes / (ms * 1e-3) / 1e9, 2)
+    print(json.dumps({"report": res}), flush=True)
+    del kc, vc, hk, hv
+    torch.cuda.empty_cache()
+
+
 def report_all(torch, ops, args):
     """One JSON line per workload other than the metric's (shorter runs)."""
     from paged_kv_cache_330_amd.workloads import PrefixSharingWorkload, make_decode_workload
@@ -382,6 +418,7 @@ def report_all(torch, ops, args):
         print(json.dumps({"report": res}), flush=True)
         del st
         torch.cuda.empty_cache()
+    swap_report(torch, ops)
     for bs in (8, 16):
         for final in (False, True):
             ws = PrefixSharingWorkload(prefix_len=args.prefix, block_size=bs)

@@ -91,6 +91,32 @@ int pkv_block_copy(void* k_cache, void* v_cache, const pkv_cache_desc* cache,
                    const int64_t* src_dst_pairs, int64_t num_pairs, void* stream);
 
 /*
+ * Whole-block transfers between two pools of the same block shape, for
+ * swapping blocks out of the device pool into host memory and back
+ * ("PagedAttention 动态内存分页", section "动态块分配与回收": when device memory
+ * runs short, inactive KV blocks are moved to CPU memory and loaded back when
+ * they are needed).
+ *
+ *   dst_k, dst_v  destination pools, laid out as dst_cache describes.
+ *   src_k, src_v  source pools, laid out as src_cache describes; read only.
+ *                 The two descriptors must agree on block_size, num_kv_heads,
+ *                 head_dim and dtype (num_blocks may differ).  Each of the four
+ *                 pools is device memory or pinned host memory mapped for the
+ *                 device (hipHostMalloc); pageable host memory is rejected with
+ *                 PKV_ERR_INVALID_ARG before anything is launched.  Source and
+ *                 destination pools must not overlap.
+ *   src_dst_pairs [num_pairs][2] int64 (block in the source pools, block in
+ *                 the destination pools), device or pinned host memory.  For
+ *                 every pair the whole K block and the whole V block are
+ *                 copied.  Destinations must be distinct.  Out-of-range ids
+ *                 are skipped and flagged in the device error word.
+ * num_pairs == 0 is a no-op.  Same-pool copies use pkv_block_copy.
+ */
+int pkv_block_transfer(void* dst_k, void* dst_v, const pkv_cache_desc* dst_cache,
+                       const void* src_k, const void* src_v, const pkv_cache_desc* src_cache,
+                       const int64_t* src_dst_pairs, int64_t num_pairs, void* stream);
+
+/*
  * Bytes of device workspace pkv_attention_decode needs for these sizes (0 when
  * none is needed); the arguments mean what they mean for that call.  Returns
  * 0 as well for arguments the call would reject (pkv_last_error() then says

@@ -12,6 +12,7 @@ from .pagedkv_oracle import (  # noqa: F401
     gather_sequence,
     softmax_attention,
     splitk_ref,
+    transfer_ref,
     widen,
     write_ref,
 )

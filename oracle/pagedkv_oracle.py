@@ -46,6 +46,7 @@ __all__ = [
     "widen",
     "write_ref",
     "copy_ref",
+    "transfer_ref",
     "gather_sequence",
     "softmax_attention",
     "decode_ref",
@@ -108,6 +109,22 @@ def copy_ref(k_cache, v_cache, pairs) -> None:
     for s, d in pairs.tolist():
         k_cache[d] = snap_k[s]
         v_cache[d] = snap_v[s]
+
+
+def transfer_ref(dst_k, dst_v, src_k, src_v, pairs) -> None:
+    """Whole-block transfers between two pools, in place on ``dst_k`` / ``dst_v``.
+
+    "PagedAttention 动态内存分页", "动态块分配与回收": under memory pressure,
+    inactive blocks are swapped out to CPU memory and loaded back when needed.
+    For every ``(src, dst)`` pair, block ``src`` of the source pools (all
+    ``block_size`` slots, K and V) becomes block ``dst`` of the destination
+    pools; nothing else changes.  The pools are distinct, so no read sees a
+    write of the same call.
+    """
+    pairs = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+    for s, d in pairs.tolist():
+        dst_k[d] = src_k[s]
+        dst_v[d] = src_v[s]
 
 
 def gather_sequence(cache, table_row, seq_len: int) -> np.ndarray:

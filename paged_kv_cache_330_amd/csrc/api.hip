@@ -106,6 +106,31 @@ int resolve_partition(int32_t partition_tokens, int32_t block_size, int32_t* par
   return PKV_OK;
 }
 
+// Device-side address of `p`: device memory as is, pinned host memory
+// through its mapping; pageable host memory and unknown pointers fail.
+int device_address(const void* p, const char* name, void** out) {
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky error of the failed query
+    return fail(PKV_ERR_INVALID_ARG, "%s is neither device memory nor pinned host memory (%s)",
+                name, hipGetErrorString(e));
+  }
+  if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged) {
+    *out = const_cast<void*>(p);
+    return PKV_OK;
+  }
+  if (attr.type == hipMemoryTypeHost && attr.devicePointer != nullptr &&
+      attr.hostPointer != nullptr) {
+    // hostPointer/devicePointer may name the allocation or `p` itself; the
+    // offset of `p` from hostPointer covers both.
+    *out = static_cast<char*>(attr.devicePointer) +
+           (static_cast<const char*>(p) - static_cast<const char*>(attr.hostPointer));
+    return PKV_OK;
+  }
+  return fail(PKV_ERR_INVALID_ARG, "%s is neither device memory nor pinned host memory", name);
+}
+
 // Schedule and workspace of one decode call, from host-known sizes only.
 struct Plan {
   int32_t part;       // partition grid: tokens per partition
@@ -192,10 +217,51 @@ int pkv_block_copy(void* k_cache, void* v_cache, const pkv_cache_desc* cache,
   PKV_TRY(error_word(&err));
   const int64_t block_bytes = static_cast<int64_t>(cache->block_size) * cache->num_kv_heads *
                               cache->head_dim * elem_bytes(cache->dtype);
-  hipError_t e = pkv::launch_block_copy(k_cache, v_cache, src_dst_pairs, num_pairs,
-                                        cache->num_blocks, block_bytes, err,
-                                        static_cast<hipStream_t>(stream));
+  hipError_t e = pkv::launch_block_copy(k_cache, v_cache, k_cache, v_cache, src_dst_pairs,
+                                        num_pairs, cache->num_blocks, cache->num_blocks,
+                                        block_bytes, err, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : hip_fail(e, "block_copy launch");
+}
+
+int pkv_block_transfer(void* dst_k, void* dst_v, const pkv_cache_desc* dst_cache,
+                       const void* src_k, const void* src_v, const pkv_cache_desc* src_cache,
+                       const int64_t* src_dst_pairs, int64_t num_pairs, void* stream) {
+  g_last_error.clear();
+  PKV_TRY(check_cache(dst_cache));
+  PKV_TRY(check_cache(src_cache));
+  if (dst_cache->block_size != src_cache->block_size ||
+      dst_cache->num_kv_heads != src_cache->num_kv_heads ||
+      dst_cache->head_dim != src_cache->head_dim || dst_cache->dtype != src_cache->dtype)
+    return fail(PKV_ERR_INVALID_ARG, "source and destination pools differ in block shape or dtype");
+  if (num_pairs < 0) return fail(PKV_ERR_INVALID_ARG, "num_pairs %lld < 0", (long long)num_pairs);
+  if (num_pairs == 0) return PKV_OK;
+  PKV_TRY(check_ptr(src_dst_pairs, 8, "src_dst_pairs"));
+  PKV_TRY(check_ptr(dst_k, 16, "dst_k"));
+  PKV_TRY(check_ptr(dst_v, 16, "dst_v"));
+  PKV_TRY(check_ptr(src_k, 16, "src_k"));
+  PKV_TRY(check_ptr(src_v, 16, "src_v"));
+  // Every pool must be memory the device can address: device memory, or
+  // pinned host memory mapped for the device (its device-side address is
+  // used).  Anything else is rejected here instead of faulting in the kernel.
+  void* dk = nullptr;
+  void* dv = nullptr;
+  const void* sk = nullptr;
+  const void* sv = nullptr;
+  PKV_TRY(device_address(dst_k, "dst_k", &dk));
+  PKV_TRY(device_address(dst_v, "dst_v", &dv));
+  PKV_TRY(device_address(src_k, "src_k", const_cast<void**>(&sk)));
+  PKV_TRY(device_address(src_v, "src_v", const_cast<void**>(&sv)));
+  void* pairs_dev = nullptr;
+  PKV_TRY(device_address(src_dst_pairs, "src_dst_pairs", &pairs_dev));
+  unsigned* err = nullptr;
+  PKV_TRY(error_word(&err));
+  const int64_t block_bytes = static_cast<int64_t>(src_cache->block_size) *
+                              src_cache->num_kv_heads * src_cache->head_dim *
+                              elem_bytes(src_cache->dtype);
+  hipError_t e = pkv::launch_block_copy(dk, dv, sk, sv, static_cast<const int64_t*>(pairs_dev),
+                                        num_pairs, src_cache->num_blocks, dst_cache->num_blocks,
+                                        block_bytes, err, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "block_transfer launch");
 }
 
 size_t pkv_attention_workspace_bytes(const pkv_cache_desc* cache, int32_t num_seqs,

@@ -93,9 +93,13 @@ hipError_t launch_kv_write(const void* k, const void* v, const int64_t* slots, i
                            void* k_cache, void* v_cache, int64_t num_slots, int64_t row_bytes,
                            unsigned* err, hipStream_t stream);
 
-hipError_t launch_block_copy(void* k_cache, void* v_cache, const int64_t* pairs,
-                             int64_t num_pairs, int64_t num_blocks, int64_t block_bytes,
-                             unsigned* err, hipStream_t stream);
+// Whole-block copies from the (src_k, src_v) pools to the (dst_k, dst_v)
+// pools, which may be the same pools (copy-on-write) or different ones
+// (swapping); every pointer must be addressable by the device.
+hipError_t launch_block_copy(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                             const int64_t* pairs, int64_t num_pairs, int64_t src_blocks,
+                             int64_t dst_blocks, int64_t block_bytes, unsigned* err,
+                             hipStream_t stream);
 
 // Chooses the kernel for (dtype, head_dim, block_size, group) and schedule
 // (a.slices > 0: balanced; else the partition grid) and launches the main

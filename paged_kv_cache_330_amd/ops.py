@@ -21,6 +21,7 @@ __all__ = [
     "load_library",
     "pkv_kv_write",
     "pkv_block_copy",
+    "pkv_block_transfer",
     "pkv_attention_workspace_bytes",
     "pkv_attention_decode",
     "pkv_check_device_errors",
@@ -69,13 +70,14 @@ def load_library() -> ctypes.CDLL:
     D = ctypes.POINTER(CacheDesc)
     lib.pkv_kv_write.argtypes = [P, P, P, I64, P, P, D, P]
     lib.pkv_block_copy.argtypes = [P, P, D, P, I64, P]
+    lib.pkv_block_transfer.argtypes = [P, P, D, P, P, D, P, I64, P]
     lib.pkv_attention_workspace_bytes.argtypes = [D, I32, I32, I32, I32]
     lib.pkv_attention_workspace_bytes.restype = SZ
     lib.pkv_attention_decode.argtypes = [P, I32, P, P, P, D, P, I32, P, I32, I32,
                                          ctypes.c_float, I32, P, SZ, P]
     lib.pkv_last_error.restype = ctypes.c_char_p
     lib.pkv_check_device_errors.argtypes = [P]
-    for name in ("pkv_kv_write", "pkv_block_copy", "pkv_attention_decode",
+    for name in ("pkv_kv_write", "pkv_block_copy", "pkv_block_transfer", "pkv_attention_decode",
                  "pkv_check_device_errors"):
         getattr(lib, name).restype = ctypes.c_int
     _LIB = lib
@@ -107,11 +109,11 @@ def _ptr(t: Optional[torch.Tensor]):
     return ctypes.c_void_p(t.data_ptr() if t is not None else 0)
 
 
-def _need(t: torch.Tensor, name: str, dtype=None, ndim=None):
+def _need(t: torch.Tensor, name: str, dtype=None, ndim=None, host_ok: bool = False):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_cuda and not (host_ok and t.is_pinned()):
+        raise ValueError(f"{name} must be a GPU tensor" + (" or pinned host memory" if host_ok else ""))
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
@@ -120,9 +122,9 @@ def _need(t: torch.Tensor, name: str, dtype=None, ndim=None):
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
 
 
-def _desc(k_cache: torch.Tensor, v_cache: torch.Tensor) -> CacheDesc:
-    _need(k_cache, "k_cache", ndim=4)
-    _need(v_cache, "v_cache", dtype=k_cache.dtype, ndim=4)
+def _desc(k_cache: torch.Tensor, v_cache: torch.Tensor, host_ok: bool = False) -> CacheDesc:
+    _need(k_cache, "k_cache", ndim=4, host_ok=host_ok)
+    _need(v_cache, "v_cache", dtype=k_cache.dtype, ndim=4, host_ok=host_ok)
     if k_cache.shape != v_cache.shape:
         raise ValueError("k_cache and v_cache shapes differ")
     if k_cache.dtype not in _DTYPES:
@@ -154,6 +156,24 @@ def pkv_block_copy(k_cache: torch.Tensor, v_cache: torch.Tensor,
         raise ValueError("src_dst_pairs must be [n, 2]")
     _check(load_library().pkv_block_copy(_ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
                                          _ptr(src_dst_pairs), src_dst_pairs.shape[0], _stream()))
+
+
+def pkv_block_transfer(dst_k: torch.Tensor, dst_v: torch.Tensor, src_k: torch.Tensor,
+                       src_v: torch.Tensor, src_dst_pairs: torch.Tensor) -> None:
+    """Copy whole blocks ``(src, dst)`` from the source pools into the destination pools.
+
+    Either side may be pinned host memory (``torch.empty(..., pin_memory=True)``):
+    swap-out is device -> host, swap-in host -> device.  ``src_dst_pairs`` is an
+    int64 ``[n, 2]`` GPU tensor.
+    """
+    dd = _desc(dst_k, dst_v, host_ok=True)
+    sd = _desc(src_k, src_v, host_ok=True)
+    _need(src_dst_pairs, "src_dst_pairs", dtype=torch.int64, ndim=2)
+    if src_dst_pairs.shape[1] != 2:
+        raise ValueError("src_dst_pairs must be [n, 2]")
+    _check(load_library().pkv_block_transfer(
+        _ptr(dst_k), _ptr(dst_v), ctypes.byref(dd), _ptr(src_k), _ptr(src_v), ctypes.byref(sd),
+        _ptr(src_dst_pairs), src_dst_pairs.shape[0], _stream()))
 
 
 def pkv_attention_workspace_bytes(k_cache: torch.Tensor, v_cache: torch.Tensor, num_seqs: int,

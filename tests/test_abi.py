@@ -45,7 +45,8 @@ def decode(lib, **kw):
 
 def test_every_declared_function_is_exported(lib):
     names = ops.declared_functions()
-    assert set(names) >= {"pkv_kv_write", "pkv_block_copy", "pkv_attention_workspace_bytes",
+    assert set(names) >= {"pkv_kv_write", "pkv_block_copy", "pkv_block_transfer",
+                          "pkv_attention_workspace_bytes",
                           "pkv_attention_decode", "pkv_last_error", "pkv_check_device_errors"}
     nm = subprocess.run(["nm", "-D", "--defined-only", ops.library_path()],
                         capture_output=True, text=True, check=True).stdout
@@ -190,3 +191,15 @@ def test_product_package_does_not_use_the_oracle():
             "print('oracle' in sys.modules)\n")
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True)
     assert r.stdout.strip() == "False"
+
+
+def test_transfer_validation(lib):
+    d = desc()
+    other = desc(hkv=4)
+    t = lib.pkv_block_transfer
+    assert t(P(), P(), ctypes.byref(d), P(), P(), ctypes.byref(d), P(), 0, P(0)) == OK
+    assert t(P(), P(), ctypes.byref(d), P(), P(), ctypes.byref(other), P(), 2, P(0)) == INVALID
+    assert "block shape" in ops.pkv_last_error()
+    assert t(P(), P(), ctypes.byref(d), P(), P(), ctypes.byref(d), P(), -1, P(0)) == INVALID
+    assert t(P(0), P(), ctypes.byref(d), P(), P(), ctypes.byref(d), P(), 2, P(0)) == INVALID
+    assert t(P(), P(), ctypes.byref(d), P(), P(FAKE + 4), ctypes.byref(d), P(), 2, P(0)) == INVALID

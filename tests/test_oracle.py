@@ -399,3 +399,23 @@ def test_each_planted_mistake_fails_a_pin(name, golden_dir):
     with np.errstate(all="ignore"):
         res = _all_pins(_as_decode_fn(**MUTANTS[name]), golden_dir)
     assert not all(res.values()), f"mistake {name!r} passed every pin: {res}"
+
+
+# --------------------------------------------------------------------------- block transfer
+def test_transfer_ref_moves_whole_blocks_between_pools():
+    # "PagedAttention 动态内存分页", "动态块分配与回收": swapped-out blocks land
+    # whole in the other pool and come back unchanged.
+    rng = np.random.default_rng(11)
+    dev_k = rng.integers(0, 1 << 16, size=(6, 4, 2, 8), dtype=np.uint16)
+    dev_v = rng.integers(0, 1 << 16, size=(6, 4, 2, 8), dtype=np.uint16)
+    host_k = np.full((3, 4, 2, 8), 0x7FC0, np.uint16)
+    host_v = np.full((3, 4, 2, 8), 0x7FC0, np.uint16)
+    before_k, before_v = dev_k.copy(), dev_v.copy()
+    oracle.transfer_ref(host_k, host_v, dev_k, dev_v, [[4, 0], [1, 2]])
+    assert np.array_equal(host_k[0], before_k[4]) and np.array_equal(host_v[2], before_v[1])
+    assert (host_k[1] == 0x7FC0).all() and (host_v[1] == 0x7FC0).all()   # untouched slot
+    assert np.array_equal(dev_k, before_k) and np.array_equal(dev_v, before_v)  # source read only
+    dev_k[4] = 0
+    dev_v[1] = 0
+    oracle.transfer_ref(dev_k, dev_v, host_k, host_v, [[0, 4], [2, 1]])   # swap back in
+    assert np.array_equal(dev_k, before_k) and np.array_equal(dev_v, before_v)

@@ -382,3 +382,53 @@ def test_workspace_reused_across_calls(ops):
         ops.pkv_check_device_errors()
         rk, rv = oracle_caches(w)
         assert_close(out.cpu().numpy(), oracle_decode(w, rk, rv), TOL["bf16"], f"batch {w.num_seqs}")
+
+
+# --------------------------------------------------------------------------- swap
+@pytest.mark.parametrize("dtype,bs", [("bf16", 16), ("f32", 8)])
+def test_block_transfer_swap_out_and_in(ops, dtype, bs):
+    # Swap blocks out of a device pool into a pinned host pool and back into
+    # other device blocks: bit-exact against the oracle, untouched bytes too.
+    rng = np.random.default_rng(bs)
+    NB, NH, Hkv, D = 48, 20, 4, 128
+    shape, hshape = (NB, bs, Hkv, D), (NH, bs, Hkv, D)
+    if dtype == "bf16":
+        dk = rng.integers(0, 1 << 16, size=shape, dtype=np.uint16)
+        dv = rng.integers(0, 1 << 16, size=shape, dtype=np.uint16)
+        hk0 = np.full(hshape, 0x7FC0, np.uint16)
+    else:
+        dk = rng.standard_normal(shape).astype(np.float32)
+        dv = rng.standard_normal(shape).astype(np.float32)
+        hk0 = np.full(hshape, np.nan, np.float32)
+    kc, vc = torch_tensor(dk, dtype, "cuda"), torch_tensor(dv, dtype, "cuda")
+    host_k = torch_tensor(hk0, dtype, "cpu").pin_memory()
+    host_v = torch_tensor(hk0.copy(), dtype, "cpu").pin_memory()
+    out_pairs = np.stack([rng.permutation(NB)[:12], rng.permutation(NH)[:12]], 1).astype(np.int64)
+    ops.pkv_block_transfer(host_k, host_v, kc, vc, torch.from_numpy(out_pairs).cuda())
+    ops.pkv_check_device_errors()
+    ref_hk, ref_hv = hk0.copy(), hk0.copy()
+    oracle.transfer_ref(ref_hk, ref_hv, dk, dv, out_pairs)
+    assert same_bits(host_k, ref_hk) and same_bits(host_v, ref_hv)
+    # swap back into blocks that are free on the device (not sources above)
+    free = np.setdiff1d(np.arange(NB), out_pairs[:, 0])[:12]
+    in_pairs = np.stack([out_pairs[:, 1], free], 1).astype(np.int64)
+    ops.pkv_block_transfer(kc, vc, host_k, host_v, torch.from_numpy(in_pairs).cuda())
+    ops.pkv_check_device_errors()
+    oracle.transfer_ref(dk, dv, ref_hk, ref_hv, in_pairs)
+    assert same_bits(kc, dk) and same_bits(vc, dv)
+
+
+def test_block_transfer_rejects_pageable_host_memory(ops):
+    # Pageable host memory is refused before any launch (no kernel touches it).
+    import ctypes
+    lib = ops.load_library()
+    pool = np.zeros((4, 16, 8, 128), np.uint16)
+    dev = torch.zeros((4, 16, 8, 128), dtype=torch.bfloat16, device="cuda")
+    pairs = torch.zeros((1, 2), dtype=torch.int64, device="cuda")
+    d = ops.CacheDesc(4, 16, 8, 128, ops.PKV_BF16)
+    rc = lib.pkv_block_transfer(ctypes.c_void_p(pool.ctypes.data), ctypes.c_void_p(pool.ctypes.data),
+                                ctypes.byref(d), ctypes.c_void_p(dev.data_ptr()),
+                                ctypes.c_void_p(dev.data_ptr()), ctypes.byref(d),
+                                ctypes.c_void_p(pairs.data_ptr()), 1, ctypes.c_void_p(0))
+    assert rc == -1 and "pinned" in ops.pkv_last_error()
+    torch.cuda.synchronize()
