@@ -167,14 +167,66 @@ int pkv_attention_decode(void* out, int32_t out_dtype, const void* q,
                          float scale, int32_t partition_tokens,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Bytes of device workspace pkv_attention_decode_shared needs (0 for arguments
+ * that call would reject, with pkv_last_error() saying why, and for
+ * num_seqs == 0).  Host-known sizes only.
+ */
+size_t pkv_attention_shared_workspace_bytes(const pkv_cache_desc* cache, int32_t num_seqs,
+                                            int32_t num_q_heads, int32_t num_groups);
+
+/*
+ * Decode-step attention for batches in which groups of sequences share a
+ * prefix of their cache ("PagedAttention 动态内存分页", section "写时复制与内存
+ * 共享": samples or beams forked from one prompt reference the prompt's
+ * physical blocks; "Paged KV", section "支持 Prefix Cache": several sequences
+ * may hold read-only references to one physical block).  The output is the
+ * one pkv_attention_decode computes for the same arguments (up to fp32
+ * rounding); the description of the groups only lets the kernels read each
+ * shared block once for the whole group instead of once per member.
+ *
+ * All arguments shared with pkv_attention_decode mean the same; the pools
+ * must be PKV_BF16 with head_dim 128, and num_seqs <= 2048.
+ *   group_offsets [num_groups + 1] int32: the members of group g are
+ *                 group_seqs[group_offsets[g] .. group_offsets[g + 1]);
+ *                 group_offsets[0] == 0, nondecreasing, last <= num_seqs.
+ *   group_seqs    int32 sequence indices in [0, num_seqs); a sequence is a
+ *                 member of at most one group, and sequences in no group are
+ *                 attended on their own.
+ *   group_lens    [num_groups] int32: shared tokens P_g of group g.  Every
+ *                 member must map each token t < P_g to the same slot, i.e.
+ *                 the first ceil(P_g / block_size) entries of the members'
+ *                 block tables are equal, and P_g <= seq_lens of every member.
+ *   num_groups    0 <= num_groups <= num_seqs (0: no sharing; the three
+ *                 group arrays are then not read and may be NULL).
+ *   workspace     pkv_attention_shared_workspace_bytes(...) bytes of scratch,
+ *                 overwritten; calls that share a workspace must not overlap.
+ * The group description lives in device memory and is checked there: offsets
+ * that do not start at 0, decrease or exceed num_seqs make the call ignore
+ * the sharing; member ids out of range, a sequence listed twice, a P_g outside
+ * [0, seq_len] of a member, or block tables that differ over the shared
+ * tokens leave the output unspecified.  Each of these is recorded in the
+ * device error word (reported by pkv_check_device_errors); no access leaves
+ * the buffers in any case.  num_seqs == 0 is a no-op.
+ */
+int pkv_attention_decode_shared(void* out, int32_t out_dtype, const void* q,
+                                const void* k_cache, const void* v_cache,
+                                const pkv_cache_desc* cache,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                float scale, const int32_t* group_offsets,
+                                const int32_t* group_seqs, const int32_t* group_lens,
+                                int32_t num_groups, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 /* Message for the last non-OK return on this thread ("" if none). */
 const char* pkv_last_error(void);
 
 /*
  * Synchronises `stream`, then reads and clears the current device's error
  * word.  Returns PKV_OK if no kernel recorded a bad slot, block id, sequence
- * length or copy pair since the last check; otherwise PKV_ERR_INVALID_ARG
- * with the offending kinds in pkv_last_error().
+ * length, copy pair or shared-prefix description since the last check;
+ * otherwise PKV_ERR_INVALID_ARG with the offending kinds in pkv_last_error().
  */
 int pkv_check_device_errors(void* stream);
 

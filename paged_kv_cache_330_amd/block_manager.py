@@ -21,6 +21,9 @@ Sources, by page title and section:
   sharer must write into it.
 * "PagedAttention 动态内存分页", "动态块分配与回收": blocks are taken lazily,
   when a token needs them, and returned to the pool as soon as a sequence ends.
+* "Paged KV", "支持 Prefix Cache": several sequences may hold read-only
+  references to one physical block; ``shared_prefix_groups`` describes such
+  sharing for ``pkv_attention_decode_shared``.
 """
 from __future__ import annotations
 
@@ -162,6 +165,39 @@ class BlockManager:
                 raise ValueError("table wider than width")
             out[i, :len(t)] = t
         return out
+
+    def shared_prefix_groups(self, seq_ids: Sequence
+                             ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+        """Groups of ``seq_ids`` that share their leading physical blocks.
+
+        Sequences whose first block is the same physical block form a group
+        (two members or more, in order of first appearance).  A group's shared
+        length is the number of leading table entries that all its members
+        have in common, in tokens, capped by its shortest member: every member
+        maps each token below it to the same slot.  Returns ``(offsets [G+1],
+        members, lens [G])`` as int32 arrays, members being indices into
+        ``seq_ids``, the layout ``pkv_attention_decode_shared`` takes.
+        """
+        by_first: Dict[int, List[int]] = {}
+        for i, s in enumerate(seq_ids):
+            table = self.tables[s]
+            if table:
+                by_first.setdefault(table[0], []).append(i)
+        offsets, members, lens = [0], [], []
+        for idx in by_first.values():
+            if len(idx) < 2:
+                continue
+            tables = [self.tables[seq_ids[i]] for i in idx]
+            width = min(len(t) for t in tables)
+            k = 0
+            while k < width and all(t[k] == tables[0][k] for t in tables):
+                k += 1
+            shortest = min(self.lengths[seq_ids[i]] for i in idx)
+            members.extend(idx)
+            offsets.append(len(members))
+            lens.append(min(k * self.block_size, shortest))
+        return (np.asarray(offsets, np.int32), np.asarray(members, np.int32),
+                np.asarray(lens, np.int32))
 
     def internal_fragmentation(self, seq_id) -> int:
         """Reserved but unused slots of one sequence (at most block_size - 1)."""

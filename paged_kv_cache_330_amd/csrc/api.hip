@@ -177,6 +177,99 @@ int make_plan(const pkv_cache_desc* cache, int32_t num_seqs, int32_t num_q_heads
   return PKV_OK;
 }
 
+// Schedule and workspace of one shared-prefix decode call.
+struct SharedPlan {
+  int32_t slices;       // slices per kv-head group
+  int64_t prefix_rows;  // partial rows of prefix pieces
+  pkv::WorkspaceLayout layout;
+  size_t workspace;
+};
+
+int make_shared_plan(const pkv_cache_desc* cache, int32_t num_seqs, int32_t num_q_heads,
+                     int32_t max_blocks_per_seq, int32_t num_groups, SharedPlan* p) {
+  Plan base;
+  PKV_TRY(make_plan(cache, num_seqs, num_q_heads, max_blocks_per_seq, 0, &base));
+  if (cache->dtype != PKV_BF16 || cache->head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "shared-prefix decode needs bf16 pools with head_dim 128");
+  const int group = num_q_heads / cache->num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return fail(PKV_ERR_UNSUPPORTED, "query group %d is not 1, 2, 4 or 8", group);
+  if (num_seqs > pkv::kMaxBalancedSeqs)
+    return fail(PKV_ERR_UNSUPPORTED, "shared-prefix decode takes at most %d sequences, got %d",
+                pkv::kMaxBalancedSeqs, num_seqs);
+  if (num_groups < 0 || num_groups > num_seqs)
+    return fail(PKV_ERR_INVALID_ARG, "num_groups %d is not in [0, num_seqs = %d]", num_groups,
+                num_seqs);
+  p->slices = pkv::balanced_slices(cache->num_kv_heads);
+  p->prefix_rows = pkv::shared_prefix_rows(num_seqs, num_groups, cache->num_kv_heads, group,
+                                           p->slices);
+  const int64_t rows = p->prefix_rows + pkv::shared_tail_rows(num_seqs, num_q_heads, p->slices);
+  p->layout = pkv::workspace_layout(rows, cache->head_dim,
+                                    static_cast<int64_t>(pkv::kSharedDescInts) * num_seqs);
+  p->workspace = num_seqs > 0 ? p->layout.total : 0;
+  return PKV_OK;
+}
+
+// Query group, output type and scale of a decode call.
+int check_decode_scalars(const pkv_cache_desc* cache, int32_t num_q_heads, int32_t out_dtype,
+                         float scale) {
+  const int group = num_q_heads / cache->num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return fail(PKV_ERR_UNSUPPORTED, "query group %d is not 1, 2, 4 or 8", group);
+  if (out_dtype != PKV_F32 && out_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "out_dtype %d is neither PKV_F32 nor PKV_BF16", out_dtype);
+  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
+    return fail(PKV_ERR_INVALID_ARG, "scale is not finite");
+  return PKV_OK;
+}
+
+// Checks shared by both decode calls; fills everything but the workspace
+// and the error word (no HIP call here).
+int fill_decode_args(void* out, int32_t out_dtype, const void* q, const void* k_cache,
+                     const void* v_cache, const pkv_cache_desc* cache,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
+                     pkv::DecodeArgs* a) {
+  PKV_TRY(check_ptr(out, 16, "out"));
+  PKV_TRY(check_ptr(q, 16, "q"));
+  PKV_TRY(check_ptr(k_cache, 16, "k_cache"));
+  PKV_TRY(check_ptr(v_cache, 16, "v_cache"));
+  PKV_TRY(check_ptr(block_tables, 4, "block_tables"));
+  PKV_TRY(check_ptr(seq_lens, 4, "seq_lens"));
+  if (cache->num_blocks < 1) return fail(PKV_ERR_INVALID_ARG, "num_blocks must be >= 1");
+  a->out = out;
+  a->q = q;
+  a->k_cache = k_cache;
+  a->v_cache = v_cache;
+  a->block_tables = block_tables;
+  a->seq_lens = seq_lens;
+  a->num_blocks = cache->num_blocks;
+  a->max_blocks_per_seq = max_blocks_per_seq;
+  a->num_seqs = num_seqs;
+  a->num_q_heads = num_q_heads;
+  a->num_kv_heads = cache->num_kv_heads;
+  a->out_bf16 = out_dtype == PKV_BF16;
+  a->scale_log2e = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
+  return PKV_OK;
+}
+
+// Points the partial-result arrays of `a` into a checked workspace.
+int attach_workspace(void* workspace, size_t workspace_bytes, size_t need,
+                     const pkv::WorkspaceLayout& layout, pkv::DecodeArgs* a) {
+  if (need == 0) return PKV_OK;
+  if (!workspace) return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
+  if (!aligned(workspace, 16)) return fail(PKV_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need,
+                workspace_bytes);
+  char* w = static_cast<char*>(workspace);
+  a->ws_desc = reinterpret_cast<int*>(w + layout.desc_off);
+  a->ws_max = reinterpret_cast<float*>(w + layout.max_off);
+  a->ws_sum = reinterpret_cast<float*>(w + layout.sum_off);
+  a->ws_acc = reinterpret_cast<float*>(w + layout.acc_off);
+  return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -282,60 +375,63 @@ int pkv_attention_decode(void* out, int32_t out_dtype, const void* q, const void
   g_last_error.clear();
   Plan plan;
   PKV_TRY(make_plan(cache, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, &plan));
-  const int group = num_q_heads / cache->num_kv_heads;
-  if (group != 1 && group != 2 && group != 4 && group != 8)
-    return fail(PKV_ERR_UNSUPPORTED, "query group %d is not 1, 2, 4 or 8", group);
-  if (out_dtype != PKV_F32 && out_dtype != PKV_BF16)
-    return fail(PKV_ERR_UNSUPPORTED, "out_dtype %d is neither PKV_F32 nor PKV_BF16", out_dtype);
-  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
-    return fail(PKV_ERR_INVALID_ARG, "scale is not finite");
+  PKV_TRY(check_decode_scalars(cache, num_q_heads, out_dtype, scale));
   if (num_seqs == 0) return PKV_OK;
-  PKV_TRY(check_ptr(out, 16, "out"));
-  PKV_TRY(check_ptr(q, 16, "q"));
-  PKV_TRY(check_ptr(k_cache, 16, "k_cache"));
-  PKV_TRY(check_ptr(v_cache, 16, "v_cache"));
-  PKV_TRY(check_ptr(block_tables, 4, "block_tables"));
-  PKV_TRY(check_ptr(seq_lens, 4, "seq_lens"));
-  if (cache->num_blocks < 1) return fail(PKV_ERR_INVALID_ARG, "num_blocks must be >= 1");
-
   pkv::DecodeArgs a{};
-  if (plan.workspace > 0) {
-    if (!workspace)
-      return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", plan.workspace);
-    if (!aligned(workspace, 16)) return fail(PKV_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
-    if (workspace_bytes < plan.workspace)
-      return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", plan.workspace,
-                  workspace_bytes);
-    char* w = static_cast<char*>(workspace);
-    a.ws_desc = reinterpret_cast<int*>(w + plan.layout.desc_off);
-    a.ws_max = reinterpret_cast<float*>(w + plan.layout.max_off);
-    a.ws_sum = reinterpret_cast<float*>(w + plan.layout.sum_off);
-    a.ws_acc = reinterpret_cast<float*>(w + plan.layout.acc_off);
-  }
-  unsigned* err = nullptr;
-  PKV_TRY(error_word(&err));
-
-  a.out = out;
-  a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.block_tables = block_tables;
-  a.seq_lens = seq_lens;
-  a.err = err;
-  a.num_blocks = cache->num_blocks;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.num_seqs = num_seqs;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = cache->num_kv_heads;
+  PKV_TRY(fill_decode_args(out, out_dtype, q, k_cache, v_cache, cache, block_tables,
+                           max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, scale, &a));
+  PKV_TRY(attach_workspace(workspace, workspace_bytes, plan.workspace, plan.layout, &a));
+  PKV_TRY(error_word(&a.err));
   a.part_tokens = plan.part;
   a.max_parts = static_cast<int32_t>(plan.max_parts);
   a.slices = plan.slices;
-  a.out_bf16 = out_dtype == PKV_BF16;
-  a.scale_log2e = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
-
   hipError_t e = pkv::launch_decode(a, cache->dtype == PKV_BF16, cache->head_dim,
-                                    cache->block_size, group, static_cast<hipStream_t>(stream));
+                                    cache->block_size, num_q_heads / cache->num_kv_heads,
+                                    static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : hip_fail(e, "attention_decode launch");
+}
+
+size_t pkv_attention_shared_workspace_bytes(const pkv_cache_desc* cache, int32_t num_seqs,
+                                            int32_t num_q_heads, int32_t num_groups) {
+  SharedPlan p;
+  if (make_shared_plan(cache, num_seqs, num_q_heads, 1, num_groups, &p) != PKV_OK) return 0;
+  return p.workspace;
+}
+
+int pkv_attention_decode_shared(void* out, int32_t out_dtype, const void* q, const void* k_cache,
+                                const void* v_cache, const pkv_cache_desc* cache,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                float scale, const int32_t* group_offsets,
+                                const int32_t* group_seqs, const int32_t* group_lens,
+                                int32_t num_groups, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  g_last_error.clear();
+  SharedPlan plan;
+  PKV_TRY(make_shared_plan(cache, num_seqs, num_q_heads, max_blocks_per_seq, num_groups, &plan));
+  PKV_TRY(check_decode_scalars(cache, num_q_heads, out_dtype, scale));
+  if (num_seqs == 0) return PKV_OK;
+  pkv::SharedArgs sa{};
+  PKV_TRY(fill_decode_args(out, out_dtype, q, k_cache, v_cache, cache, block_tables,
+                           max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, scale, &sa.d));
+  if (num_groups > 0) {
+    PKV_TRY(check_ptr(group_offsets, 4, "group_offsets"));
+    PKV_TRY(check_ptr(group_seqs, 4, "group_seqs"));
+    PKV_TRY(check_ptr(group_lens, 4, "group_lens"));
+  }
+  PKV_TRY(attach_workspace(workspace, workspace_bytes, plan.workspace, plan.layout, &sa.d));
+  PKV_TRY(error_word(&sa.d.err));
+  sa.d.slices = plan.slices;
+  sa.group_offsets = group_offsets;
+  sa.group_seqs = group_seqs;
+  sa.group_lens = group_lens;
+  sa.num_groups = num_groups;
+  sa.min_chunks = PKV_SHARED_MIN_CHUNKS;
+  sa.prefix_rows = plan.prefix_rows;
+  hipError_t e = pkv::launch_shared_decode(sa, cache->block_size,
+                                           num_q_heads / cache->num_kv_heads,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "attention_decode_shared launch");
 }
 
 int pkv_check_device_errors(void* stream) {
@@ -351,11 +447,12 @@ int pkv_check_device_errors(void* stream) {
   const unsigned zero = 0;
   e = hipMemcpy(err, &zero, sizeof(zero), hipMemcpyHostToDevice);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpy(clear error word)");
-  return fail(PKV_ERR_INVALID_ARG, "device range checks failed:%s%s%s%s",
+  return fail(PKV_ERR_INVALID_ARG, "device range checks failed:%s%s%s%s%s",
               (word & pkv::kErrSlot) ? " slot>=num_blocks*block_size" : "",
               (word & pkv::kErrBlockId) ? " block_id_out_of_range" : "",
               (word & pkv::kErrSeqLen) ? " seq_len_out_of_range" : "",
-              (word & pkv::kErrCopyPair) ? " copy_pair_out_of_range" : "");
+              (word & pkv::kErrCopyPair) ? " copy_pair_out_of_range" : "",
+              (word & pkv::kErrShared) ? " shared_prefix_inconsistent" : "");
 }
 
 }  // extern "C"

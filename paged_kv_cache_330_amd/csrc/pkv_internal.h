@@ -14,6 +14,7 @@ enum : unsigned {
   kErrBlockId = 2u,    // block-table entry outside [0, num_blocks)
   kErrSeqLen = 4u,     // seq_len < 0 or > max_blocks_per_seq * block_size
   kErrCopyPair = 8u,   // copy src/dst outside [0, num_blocks)
+  kErrShared = 16u,    // shared-prefix description disagrees with the tables or lengths
 };
 
 constexpr int kDefaultPartitionTokens = 512;
@@ -41,6 +42,9 @@ constexpr int kMaxBalancedSeqs = 2048;     // batch limit of the balanced schedu
 #endif
 #ifndef PKV_BALANCED_WGS
 #define PKV_BALANCED_WGS 256    // workgroups of the balanced schedule (all kv-head groups)
+#endif
+#ifndef PKV_SHARED_MIN_CHUNKS
+#define PKV_SHARED_MIN_CHUNKS 1 // shared-prefix schedule: fewest 16-token chunks per slice
 #endif
 
 // Waves per workgroup of the matrix-core kernels: one per kv head, the
@@ -110,5 +114,37 @@ hipError_t launch_decode(const DecodeArgs& a, int bf16, int head_dim, int block_
 
 // The bf16 head_dim-128 kernels of either schedule (attention_mfma.hip).
 hipError_t launch_mfma_decode(const DecodeArgs& a, int block_size, int group, hipStream_t stream);
+
+// Decode with shared prefixes (attention_shared.hip).  A prefix stream reads
+// a group's shared blocks once for up to 16 * kSharedSets query columns, i.e.
+// shared_members_per_stream(G) sequences of query group G.
+constexpr int kSharedSets = 2;
+inline int shared_members_per_stream(int group) { return 16 * kSharedSets / group; }
+
+// Partial-result rows of the shared-prefix schedule: prefix pieces first,
+// [NG + ceil(B / members) + slices][Hkv][16 * kSharedSets], then tail pieces,
+// [B + slices][Hkv][G].
+inline int64_t shared_prefix_rows(int num_seqs, int num_groups, int num_kv_heads, int group,
+                                  int slices) {
+  const int m = shared_members_per_stream(group);
+  return (static_cast<int64_t>(num_groups) + (num_seqs + m - 1) / m + slices) * num_kv_heads *
+         (16 * kSharedSets);
+}
+inline int64_t shared_tail_rows(int num_seqs, int num_q_heads, int slices) {
+  return (static_cast<int64_t>(num_seqs) + slices) * num_q_heads;
+}
+constexpr int kSharedDescInts = 8;  // merge descriptor ints per sequence
+
+struct SharedArgs {
+  DecodeArgs d;                  // d.slices: slices per kv-head group; d.ws_desc: descriptors
+  const int32_t* group_offsets;  // [num_groups + 1]: members of group g are
+  const int32_t* group_seqs;     //   group_seqs[group_offsets[g] .. group_offsets[g + 1])
+  const int32_t* group_lens;     // [num_groups]: tokens every member maps to the same slots
+  int32_t num_groups;
+  int32_t min_chunks;            // fewest 16-token chunks per slice
+  int64_t prefix_rows;           // partial rows of prefix pieces; tail rows follow
+};
+
+hipError_t launch_shared_decode(const SharedArgs& a, int block_size, int group, hipStream_t stream);
 
 }  // namespace pkv

@@ -24,6 +24,8 @@ __all__ = [
     "pkv_block_transfer",
     "pkv_attention_workspace_bytes",
     "pkv_attention_decode",
+    "pkv_attention_shared_workspace_bytes",
+    "pkv_attention_decode_shared",
     "pkv_check_device_errors",
     "pkv_last_error",
     "PKV_F32",
@@ -75,10 +77,14 @@ def load_library() -> ctypes.CDLL:
     lib.pkv_attention_workspace_bytes.restype = SZ
     lib.pkv_attention_decode.argtypes = [P, I32, P, P, P, D, P, I32, P, I32, I32,
                                          ctypes.c_float, I32, P, SZ, P]
+    lib.pkv_attention_shared_workspace_bytes.argtypes = [D, I32, I32, I32]
+    lib.pkv_attention_shared_workspace_bytes.restype = SZ
+    lib.pkv_attention_decode_shared.argtypes = [P, I32, P, P, P, D, P, I32, P, I32, I32,
+                                                ctypes.c_float, P, P, P, I32, P, SZ, P]
     lib.pkv_last_error.restype = ctypes.c_char_p
     lib.pkv_check_device_errors.argtypes = [P]
     for name in ("pkv_kv_write", "pkv_block_copy", "pkv_block_transfer", "pkv_attention_decode",
-                 "pkv_check_device_errors"):
+                 "pkv_attention_decode_shared", "pkv_check_device_errors"):
         getattr(lib, name).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -218,6 +224,66 @@ def pkv_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tens
         _ptr(out), _DTYPES[out.dtype], _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
         _ptr(block_tables), mb, _ptr(seq_lens), B, Hq, float(scale), partition_tokens,
         _ptr(workspace), wbytes, _stream()))
+    return out
+
+
+def pkv_attention_shared_workspace_bytes(k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                         num_seqs: int, num_q_heads: int, num_groups: int) -> int:
+    """Workspace bytes ``pkv_attention_decode_shared`` needs for these pools and sizes."""
+    desc = _desc(k_cache, v_cache)
+    return int(load_library().pkv_attention_shared_workspace_bytes(
+        ctypes.byref(desc), num_seqs, num_q_heads, num_groups))
+
+
+def pkv_attention_decode_shared(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                                v_cache: torch.Tensor, block_tables: torch.Tensor,
+                                seq_lens: torch.Tensor, scale: float,
+                                group_offsets: Optional[torch.Tensor],
+                                group_seqs: Optional[torch.Tensor],
+                                group_lens: Optional[torch.Tensor],
+                                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode attention for sequences that share prefixes; returns ``out``.
+
+    The result is that of ``pkv_attention_decode`` on the same arguments.
+    ``group_offsets`` ``[G + 1]``, ``group_seqs`` and ``group_lens`` ``[G]`` are
+    int32 GPU tensors describing the groups (all three may be ``None`` for no
+    group); ``workspace`` is allocated through torch when not given.
+    """
+    desc = _desc(k_cache, v_cache)
+    _need(q, "q", dtype=k_cache.dtype, ndim=3)
+    _need(out, "out", ndim=3)
+    if out.dtype not in _DTYPES:
+        raise TypeError("out must be float32 or bfloat16")
+    _need(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _need(seq_lens, "seq_lens", dtype=torch.int32, ndim=1)
+    B, Hq, D = q.shape
+    if tuple(out.shape) != (B, Hq, D) or D != desc.head_dim:
+        raise ValueError("out/q shapes do not match [B, Hq, head_dim]")
+    if block_tables.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("block_tables/seq_lens must have B rows")
+    groups = (group_offsets, group_seqs, group_lens)
+    if any(g is None for g in groups):
+        if not all(g is None for g in groups):
+            raise ValueError("give all three group tensors or none")
+        ng = 0
+    else:
+        _need(group_offsets, "group_offsets", dtype=torch.int32, ndim=1)
+        _need(group_seqs, "group_seqs", dtype=torch.int32, ndim=1)
+        _need(group_lens, "group_lens", dtype=torch.int32, ndim=1)
+        ng = group_lens.shape[0]
+        if group_offsets.shape[0] != ng + 1:
+            raise ValueError("group_offsets must have len(group_lens) + 1 entries")
+    mb = block_tables.shape[1]
+    need = int(load_library().pkv_attention_shared_workspace_bytes(ctypes.byref(desc), B, Hq, ng))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _need(workspace, "workspace")
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load_library().pkv_attention_decode_shared(
+        _ptr(out), _DTYPES[out.dtype], _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
+        _ptr(block_tables), mb, _ptr(seq_lens), B, Hq, float(scale), _ptr(group_offsets),
+        _ptr(group_seqs), _ptr(group_lens), ng, _ptr(workspace), wbytes, _stream()))
     return out
 
 

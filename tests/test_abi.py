@@ -203,3 +203,56 @@ def test_transfer_validation(lib):
     assert t(P(), P(), ctypes.byref(d), P(), P(), ctypes.byref(d), P(), -1, P(0)) == INVALID
     assert t(P(0), P(), ctypes.byref(d), P(), P(), ctypes.byref(d), P(), 2, P(0)) == INVALID
     assert t(P(), P(), ctypes.byref(d), P(), P(FAKE + 4), ctypes.byref(d), P(), 2, P(0)) == INVALID
+
+
+def shared(lib, **kw):
+    a = dict(out=P(), out_dtype=0, q=P(), k=P(), v=P(), desc=desc(), bt=P(), mb=32, sl=P(),
+             B=32, Hq=32, scale=0.088, go=P(), gs=P(), gl=P(), ng=4, ws=P(), wsb=1 << 30)
+    a.update(kw)
+    return lib.pkv_attention_decode_shared(
+        a["out"], a["out_dtype"], a["q"], a["k"], a["v"], ctypes.byref(a["desc"]), a["bt"],
+        a["mb"], a["sl"], a["B"], a["Hq"], a["scale"], a["go"], a["gs"], a["gl"], a["ng"],
+        a["ws"], a["wsb"], P(0))
+
+
+def shared_ws(lib, d, B, Hq, ng):
+    return lib.pkv_attention_shared_workspace_bytes(ctypes.byref(d), B, Hq, ng)
+
+
+def shared_bytes(B, hq, hkv, ng, slices, d=128):
+    # merge descriptors (8 ints per sequence); prefix pieces: up to
+    # ng + ceil(B / members) streams plus one piece per slice, 32 query columns
+    # per kv head; tail pieces: B + slices, one row per query head
+    members = 32 // (hq // hkv)
+    rows = (ng + -(-B // members) + slices) * hkv * 32 + (B + slices) * hq
+    return up(8 * B * 4) + 2 * up(rows * 4) + up(rows * d * 4)
+
+
+def test_workspace_size_shared_prefix(lib):
+    # slices per kv-head group: the balanced schedule's 256 workgroups
+    for B, hq, hkv, ng in ((32, 32, 8, 4), (1, 8, 8, 0), (2048, 64, 8, 100), (300, 16, 16, 7)):
+        d = desc(hkv=hkv)
+        slices = 256 // (hkv // 8)
+        assert shared_ws(lib, d, B, hq, ng) == shared_bytes(B, hq, hkv, ng, slices), (B, hq, ng)
+    assert shared_ws(lib, desc(), 0, 32, 0) == 0        # empty batch
+    assert shared_ws(lib, desc(), 2049, 32, 0) == 0     # above 2048 sequences
+    assert shared_ws(lib, desc(), 8, 32, 9) == 0        # more groups than sequences
+    assert shared_ws(lib, desc(dtype=0), 8, 32, 1) == 0  # fp32 pools
+    assert shared_ws(lib, desc(d=64), 8, 32, 1) == 0     # head_dim 64
+
+
+def test_shared_prefix_validation(lib):
+    assert shared(lib, B=0, ng=0, out=P(0), q=P(0)) == OK          # no-op
+    assert shared(lib, desc=desc(dtype=0)) == UNSUPPORTED
+    assert "bf16" in ops.pkv_last_error()
+    assert shared(lib, desc=desc(d=64)) == UNSUPPORTED
+    assert shared(lib, B=2049) == UNSUPPORTED
+    assert shared(lib, ng=33) == INVALID
+    assert shared(lib, ng=-1) == INVALID
+    assert shared(lib, Hq=24) == UNSUPPORTED                       # group 3
+    assert shared(lib, scale=float("inf")) == INVALID
+    assert shared(lib, go=P(0)) == INVALID
+    assert shared(lib, gl=P(FAKE + 2)) == INVALID
+    assert shared(lib, ws=P(0)) == WORKSPACE
+    need = shared_ws(lib, desc(), 32, 32, 4)
+    assert shared(lib, wsb=need - 1) == WORKSPACE

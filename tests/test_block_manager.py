@@ -7,7 +7,10 @@
   external fragmentation ("Paged KV", 收益分析; "PagedAttention 动态内存分页",
   块粒度与块表: at most 15 wasted tokens at block size 16);
 * memory of forked samples is prompt + forked parts, not samples x prompt;
-* an empty pool raises instead of over-committing.
+* an empty pool raises instead of over-committing;
+* the shared-prefix groups handed to the shared decode: every member maps each
+  token below the group's shared length to the same slot ("Paged KV",
+  支持 Prefix Cache), and the length is the longest with that property.
 """
 import json
 import math
@@ -161,3 +164,97 @@ def test_workload_shapes_match_their_description():
     assert 800 <= np.median(w3.seq_lens) <= 1300
     assert w3.num_blocks == math.ceil(1.1 * sum(math.ceil(int(L) / 16) for L in w3.seq_lens))
     assert w3.q.dtype == np.uint16
+
+
+def test_shared_prefix_groups_hand_worked():
+    # bs 4.  "a" holds 10 tokens (blocks 0, 1, 2); "b" and "c" fork from it
+    # after 10 tokens; "b" then appends 1 (copies block 2: 8 shared tokens),
+    # "c" appends nothing more.  "d" is alone.  "e" forks from "d" at 3 tokens
+    # and both append: block 3 is partial, so "e" copies it (0 shared blocks).
+    m = BlockManager(16, 4)
+    m.add_sequence("a")
+    m.append_tokens("a", 10)
+    m.fork("a", "b")
+    m.fork("a", "c")
+    m.append_tokens("b", 1)
+    m.add_sequence("d")
+    m.append_tokens("d", 3)
+    m.fork("d", "e")
+    m.append_tokens("e", 1)
+    m.append_tokens("d", 1)
+    m.add_sequence("f")
+    m.append_tokens("f", 5)
+    offsets, members, lens = m.shared_prefix_groups(["a", "b", "c", "d", "e", "f"])
+    # group of a, b, c: blocks 0 and 1 in common -> 8 tokens; d and e share no
+    # block any more (e copied block 3 before writing) -> no group
+    assert offsets.tolist() == [0, 3]
+    assert members.tolist() == [0, 1, 2]
+    assert lens.tolist() == [8]
+    # without "b" the group a, c shares all three blocks, capped at 10 tokens
+    offsets, members, lens = m.shared_prefix_groups(["c", "f", "a"])
+    assert offsets.tolist() == [0, 2] and members.tolist() == [0, 2] and lens.tolist() == [10]
+
+
+@pytest.mark.parametrize("prefix,bs,expect", [(2044, 8, 2040), (2044, 16, 2032), (2048, 16, 2048),
+                                              (2048, 8, 2048)])
+def test_shared_prefix_groups_of_parallel_sampling(prefix, bs, expect):
+    w = PrefixSharingWorkload(prefix_len=prefix, block_size=bs, tail_len=3)
+    w.prefill()
+    offsets, members, lens = w.manager.shared_prefix_groups(w.seq_ids)
+    assert offsets.tolist() == [0, 8, 16, 24, 32] and lens.tolist() == [prefix] * 4
+    for _ in range(3):
+        st = w.next_step()
+        offsets, members, lens = w.manager.shared_prefix_groups(w.seq_ids)
+        assert offsets.tolist() == [0, 8, 16, 24, 32]
+        assert members.tolist() == list(range(32))
+        assert lens.tolist() == [expect] * 4
+        for g in range(4):
+            rows = st.block_tables[members[offsets[g]:offsets[g + 1]]]
+            n = -(-expect // bs)
+            assert (rows[:, :n] == rows[0, :n]).all()          # same slots below the length
+            if expect % bs == 0 and n < rows.shape[1]:
+                assert not (rows[:, n] == rows[0, n]).all()    # and the next block differs
+
+
+def test_shared_prefix_groups_random_forks():
+    # Random fork trees: the property (same slots below the length, no longer
+    # length has it) is checked against the tables by brute force.
+    rng = np.random.default_rng(7)
+    for trial in range(20):
+        bs = int(rng.choice([4, 8, 16]))
+        m = BlockManager(4000, bs, rng.permutation(4000))
+        ids = []
+        for r in range(int(rng.integers(1, 4))):
+            root = ("r", trial, r)
+            m.add_sequence(root)
+            m.append_tokens(root, int(rng.integers(1, 60)))
+            ids.append(root)
+            for j in range(int(rng.integers(0, 5))):
+                child = ("c", trial, r, j)
+                m.fork(ids[int(rng.integers(len(ids) - j - 1, len(ids)))] if j else root, child)
+                ids.append(child)
+        for s in ids:
+            m.append_tokens(s, int(rng.integers(0, 20)))
+        order = [ids[i] for i in rng.permutation(len(ids))]
+        offsets, members, lens = m.shared_prefix_groups(order)
+        seen = set()
+        for g in range(len(lens)):
+            grp = [order[i] for i in members[offsets[g]:offsets[g + 1]]]
+            assert len(grp) >= 2 and not (set(grp) & seen)
+            seen |= set(grp)
+
+            def slots(s, n):
+                t = m.block_table(s)
+                return [t[i // bs] * bs + i % bs for i in range(n)]
+            L = int(lens[g])
+            assert L <= min(m.lengths[s] for s in grp)
+            assert all(slots(s, L) == slots(grp[0], L) for s in grp)
+            if L < min(m.lengths[s] for s in grp):
+                ext = [slots(s, L + 1)[-1] for s in grp]
+                assert len(set(ext)) > 1
+        # sequences in no group share no first block with another sequence
+        firsts = {}
+        for s in order:
+            firsts.setdefault(m.block_table(s)[0], []).append(s)
+        for blk, seqs in firsts.items():
+            assert (len(seqs) >= 2) == all(s in seen for s in seqs)

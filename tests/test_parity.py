@@ -7,7 +7,9 @@
 * GPU results are bit-identical under any relabelling of physical blocks;
 * one cached token gives exactly its V row; a zero-length sequence a zero row;
 * full-size workloads in the benchmark's launch configuration are checked on
-  sampled sequences.
+  sampled sequences;
+* the parallel-sampling workload is decoded both plainly and with its shared
+  prefixes described (pkv_attention_decode_shared), every row against the oracle.
 Unused slots and free blocks hold NaN throughout, so any read of them shows.
 """
 import functools
@@ -360,6 +362,18 @@ def test_prefix_sharing_copy_on_write(ops, prefix, bs):
             ref = oracle.decode_ref(st.q[rows], rk, rv, st.block_tables[rows], st.seq_lens[rows],
                                     ws.scale, "bf16")
             assert_close(out.cpu().numpy()[rows], ref, TOL["bf16"], f"step {s}")
+            # the shared-prefix decode, groups from the block manager, on every row
+            groups = [torch.from_numpy(a).to(dev)
+                      for a in ws.manager.shared_prefix_groups(ws.seq_ids)]
+            out_s = torch.empty_like(out)
+            ops.pkv_attention_decode_shared(out_s, torch_tensor(st.q, "bf16", dev), kc, vc,
+                                            torch.from_numpy(st.block_tables).to(dev),
+                                            torch.from_numpy(st.seq_lens).to(dev),
+                                            float(ws.scale), *groups)
+            ops.pkv_check_device_errors()
+            ref_all = oracle.decode_ref(st.q, rk, rv, st.block_tables, st.seq_lens, ws.scale,
+                                        "bf16")
+            assert_close(out_s.cpu().numpy(), ref_all, TOL["bf16"], f"step {s} shared prefix")
             # each sample's paged view equals its logical prefix + tail
             for b in rows:
                 k_log, _ = ws.logical_tokens(b, int(st.seq_lens[b]))

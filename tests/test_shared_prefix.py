@@ -1,0 +1,234 @@
+"""GPU parity of the shared-prefix decode (pkv_attention_decode_shared) with
+the fp64 oracle.
+
+Sharing changes only how often shared blocks are read, not the result, so
+the oracle is the plain decode definition (oracle.decode_ref) over the same
+block tables; the bar is that of the plain decode (max-abs 2e-3, bf16
+inputs, fp32 output).  Batches come from fork trees built with the block
+manager: groups of 1 .. 2 M + 1 members (M = sequences per prefix stream),
+prefixes shorter than a chunk, a block or a load window, members whose tail is
+empty, sequences in no group, zero lengths, and members listed in any order.
+Slots no sequence reaches hold NaN, so a read of one shows.  Inconsistent
+group descriptions must be flagged in the device error word.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+from paged_kv_cache_330_amd.block_manager import BlockManager
+from paged_kv_cache_330_amd.workloads import bf16_round, torch_tensor
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+D = 128
+
+
+@pytest.fixture(scope="module")
+def ops():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from paged_kv_cache_330_amd import ops as _ops
+    _ops.load_library()
+    return _ops
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+class Batch:
+    """Fork trees in a paged pool: ``groups`` = [(prefix_len, [tail lens])],
+    member 0 is the prompt's own sequence; ``solos`` = lengths of sequences
+    forked from nothing."""
+
+    def __init__(self, seed, bs, heads, groups, solos=(), table_pad=0):
+        rng = np.random.default_rng(seed)
+        self.bs, (self.hq, self.hkv) = bs, heads
+        need = sum(-(-(p + t) // bs) for p, tails in groups for t in tails) + \
+            sum(-(-L // bs) for L in solos) + 4
+        m = BlockManager(need, bs, rng.permutation(need))
+        ids, values = [], {}
+        for gi, (p, tails) in enumerate(groups):
+            root = ("g", gi, 0)
+            m.add_sequence(root)
+            m.append_tokens(root, p)
+            members = [root] + [("g", gi, j) for j in range(1, len(tails))]
+            for s in members[1:]:
+                m.fork(root, s)
+            kv = bf16_round(rng.standard_normal((2, p, self.hkv, D), dtype=np.float32))
+            for s, t in zip(members, tails):
+                m.append_tokens(s, t)
+                own = bf16_round(rng.standard_normal((2, t, self.hkv, D), dtype=np.float32))
+                values[s] = np.concatenate([kv, own], axis=1)
+            ids += members
+        for i, L in enumerate(solos):
+            s = ("s", i)
+            m.add_sequence(s)
+            m.append_tokens(s, L)
+            values[s] = bf16_round(rng.standard_normal((2, L, self.hkv, D), dtype=np.float32))
+            ids.append(s)
+        self.ids = [ids[i] for i in rng.permutation(len(ids))]
+        self.manager = m
+        self.B = len(self.ids)
+        width = max(len(m.block_table(s)) for s in self.ids) + table_pad
+        self.tables = m.tables_array(self.ids, width=max(width, 1))
+        self.lens = np.array([m.lengths[s] for s in self.ids], np.int32)
+        # pools: NaN everywhere but the slots some sequence reaches
+        self.k = np.full((need, bs, self.hkv, D), 0x7FC0, np.uint16)
+        self.v = self.k.copy()
+        for b, s in enumerate(self.ids):
+            t = np.arange(self.lens[b])
+            blk, off = self.tables[b, t // bs], t % bs
+            self.k[blk, off] = values[s][0]
+            self.v[blk, off] = values[s][1]
+        # bf16 bit patterns throughout (bf16_round returns uint16)
+        self.q_bits = bf16_round(rng.standard_normal((self.B, self.hq, D), dtype=np.float32))
+        self.scale = np.float32(1.0 / np.sqrt(D))
+        self.groups = m.shared_prefix_groups(self.ids)
+
+    def reference(self, rows=None):
+        rows = np.arange(self.B) if rows is None else np.asarray(rows)
+        return oracle.decode_ref(self.q_bits[rows], self.k, self.v, self.tables[rows],
+                                 self.lens[rows], self.scale, "bf16")
+
+    def device(self):
+        dev = "cuda"
+        return dict(q=torch_tensor(self.q_bits, "bf16", dev), k=torch_tensor(self.k, "bf16", dev),
+                    v=torch_tensor(self.v, "bf16", dev),
+                    bt=torch.from_numpy(self.tables).to(dev), sl=torch.from_numpy(self.lens).to(dev))
+
+
+def run_shared(ops, t, batch, groups, out_dtype=torch.float32, workspace=None, check=True):
+    out = torch.full((batch.B, batch.hq, D), 7.0, dtype=out_dtype, device="cuda")
+    g = [None, None, None] if groups is None else \
+        [torch.from_numpy(np.asarray(a, np.int32)).cuda() for a in groups]
+    ops.pkv_attention_decode_shared(out, t["q"], t["k"], t["v"], t["bt"], t["sl"],
+                                    float(batch.scale), *g, workspace=workspace)
+    if check:
+        ops.pkv_check_device_errors()
+    return out
+
+
+def assert_close(gpu, ref, what, tol=TOL):
+    gpu = gpu.astype(np.float64)
+    assert np.isfinite(gpu).all(), f"{what}: non-finite output"
+    err = np.abs(gpu - ref).max()
+    say(f"  {what}: max abs err {err:.3e} (tol {tol:g})")
+    assert err <= tol, f"{what}: max abs error {err} > {tol}"
+
+
+CASES = [
+    # id, seed, block size, (Hq, Hkv), groups, solos
+    ("gqa4_bs16", 1, 16, (32, 8), [(2044, [256] * 8), (100, [0, 5, 17, 300])], [0, 1, 40, 900]),
+    ("gqa4_bs8", 2, 8, (32, 8), [(2044, [256] * 8), (100, [0, 5, 17, 300])], [0, 1, 40, 900]),
+    ("gqa4_members_7_9_17", 3, 16, (32, 8), [(600, [1] * 7), (333, [20] * 9), (64, [2] * 17)], [5]),
+    ("mha_bs16_33_members", 4, 16, (32, 32), [(700, [3] * 33)], [5, 2000]),
+    ("gqa2_bs32", 5, 32, (16, 8), [(1000, [10] * 16 + [1]), (33, [40, 0])], [77]),
+    ("gqa8_bs64_long_prefix", 6, 64, (64, 8), [(4160, [1, 2, 3, 4, 5])], [3000]),
+    ("prefix_below_a_chunk", 7, 8, (32, 8), [(15, [3, 3]), (16, [0, 1])], [0]),
+    ("gqa4_hkv4", 8, 16, (16, 4), [(900, [50] * 5)], [17, 0, 4100]),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_shared_decode_matches_oracle(ops, case):
+    name, seed, bs, heads, groups, solos = case
+    say(f"case {name}")
+    batch = Batch(seed, bs, heads, groups, solos, table_pad=3)
+    off, mem, lens = batch.groups
+    say(f"  B={batch.B} groups={len(lens)} shared={lens.tolist()}")
+    t = batch.device()
+    out = run_shared(ops, t, batch, batch.groups)
+    ref = batch.reference()
+    assert_close(out.cpu().numpy(), ref, name)
+    # the plain decode on the same arguments agrees with it
+    plain = torch.empty_like(out)
+    ops.pkv_attention_decode(plain, t["q"], t["k"], t["v"], t["bt"], t["sl"], float(batch.scale))
+    ops.pkv_check_device_errors()
+    assert_close(out.cpu().numpy(), plain.cpu().numpy().astype(np.float64), "vs plain decode")
+
+
+def test_shared_decode_hand_described_groups(ops):
+    # Groups given by hand rather than by the block manager: a single member
+    # whose whole sequence is the "prefix" (empty tail), a group that declares
+    # less than it shares (37 tokens -> a 32-token prefix stream), a shared
+    # length of 0, and members listed in reverse order.
+    batch = Batch(11, 16, (32, 8), [(300, [0, 9, 40]), (210, [5, 6])], [77, 1])
+    bt, L = batch.tables, batch.lens
+    ids = batch.ids
+    g0 = [ids.index(("g", 0, j)) for j in (2, 1, 0)]
+    g1 = [ids.index(("g", 1, j)) for j in (1, 0)]
+    solo = ids.index(("s", 0))
+    offsets = [0, 1, 4, 6]
+    members = [solo] + g0 + g1
+    lens = [int(L[solo]), 37, 0]
+    t = batch.device()
+    out = run_shared(ops, t, batch, (offsets, members, lens))
+    assert_close(out.cpu().numpy(), batch.reference(), "hand-described groups")
+    assert (bt[g0][:, :2] == bt[g0[0], :2]).all()
+
+
+def test_shared_decode_without_groups(ops):
+    # No group at all: every sequence is its own tail stream (zero lengths,
+    # one-token sequences, sequences cut across many slices).
+    batch = Batch(12, 16, (32, 8), [], [0, 1, 16, 17, 5000, 0, 33, 2100, 1])
+    t = batch.device()
+    for groups in (None, ([0], [], [])):
+        out = run_shared(ops, t, batch, groups if groups is None else
+                         (np.array([0], np.int32), np.zeros(0, np.int32), np.zeros(0, np.int32)))
+        got = out.cpu().numpy()
+        assert_close(got, batch.reference(), "no groups")
+        for b in np.flatnonzero(batch.lens == 0):
+            assert (got[b] == 0).all()
+
+
+def test_shared_decode_bf16_output(ops):
+    batch = Batch(13, 8, (32, 8), [(500, [20] * 8)], [3])
+    t = batch.device()
+    out = run_shared(ops, t, batch, batch.groups, out_dtype=torch.bfloat16)
+    got = out.float().cpu().numpy().astype(np.float64)
+    ref = batch.reference()
+    # bf16 rounding of the output adds at most half an ulp of |ref| (< 2^-8 |ref|)
+    assert_close(got, ref, "bf16 output", tol=TOL + float(np.abs(ref).max()) * 2.0 ** -8)
+
+
+def test_shared_decode_workspace_reuse(ops):
+    # One workspace for a large then a small call: nothing from the first call
+    # may leak into the second.
+    big = Batch(14, 16, (32, 8), [(3000, [100] * 9), (50, [1] * 3)], [4000, 2, 0])
+    small = Batch(15, 16, (32, 8), [(400, [3] * 2)], [8])
+    ws = torch.empty(1 << 27, dtype=torch.uint8, device="cuda")
+    for batch in (big, small, big):
+        t = batch.device()
+        out = run_shared(ops, t, batch, batch.groups, workspace=ws)
+        assert_close(out.cpu().numpy(), batch.reference(), f"batch of {batch.B}")
+
+
+def test_shared_decode_flags_inconsistent_descriptions(ops):
+    # Every inconsistency is recorded in the device error word and no access
+    # leaves the buffers.  Offsets that are not a valid CSR make the call
+    # ignore the sharing, so its output is still the plain decode's.
+    batch = Batch(16, 16, (32, 8), [(200, [10, 20, 30])], [150, 60])
+    t = batch.device()
+    off, mem, lens = (a.tolist() for a in batch.groups)
+    a, b_ = batch.ids.index(("s", 0)), batch.ids.index(("s", 1))
+    bad = {
+        "offsets_not_from_0": ([1, 3], mem, lens, True),
+        "offsets_decrease": ([0, 3, 2], mem, lens + [16], True),
+        "offsets_past_batch": ([0, 99], mem, lens, True),
+        "member_out_of_range": (off, mem[:2] + [999], lens, False),
+        "member_listed_twice": (off, [mem[0], mem[1], mem[0]], lens, False),
+        "length_above_member": ([0, 2], [a, b_], [100], False),
+        "tables_differ": ([0, 2], [a, b_], [48], False),
+    }
+    for name, (o, m, l, plain) in bad.items():
+        say(f"  {name}")
+        out = run_shared(ops, t, batch, (o, m, l), check=False)
+        with pytest.raises(ops.PagedKVError, match="shared_prefix_inconsistent"):
+            ops.pkv_check_device_errors()
+        if plain:
+            assert_close(out.cpu().numpy(), batch.reference(), name)
+    ops.pkv_check_device_errors()  # cleared
