@@ -364,46 +364,38 @@ __device__ __forceinline__ void load_query(const DecodeArgs& a, int b, int kvh, 
 }
 
 // Streams tokens [begin, end) of one window through this wave's state, tile
-// by tile.  The loads of the next tile are issued before the current tile is
-// computed and reach the next iteration through `cur`, so a tile's loads are
-// always in flight during the compute.  Past the window's end they re-read its
-// last chunk and are never used.
+// by tile.  Two register buffers alternate (the loop is unrolled by two), so
+// that the loads of the next tile are issued before the current tile is
+// computed and stay in flight during the whole compute: with a single
+// loop-carried buffer the back edge copies the just-loaded registers, which
+// makes the wave wait for those loads at the end of every iteration.  The
+// scheduling barriers keep the loads ahead of the compute.  Past the window's
+// end the loads re-read its last chunk (or the query row) and are never used.
 template <int BS, int TC, int NS, class State>
 __device__ __forceinline__ void stream_window(const DecodeArgs& a, const TileCtx& c, int begin,
                                               const bf16x8_t (&qop)[NS][4], State& st) {
   constexpr int TILE = 16 * TC;
   int t0 = begin;
-  KVTile<TC> cur;
-  load_tile<BS, TC>(cur, t0, c);
-#if PKV_PREFETCH_TILES >= 2
-  KVTile<TC> n1;
-  load_tile<BS, TC>(n1, t0 + TILE, c);
-#endif
-  // The first tile(s) pass through an empty asm so that the loop-carried
-  // buffers are not loads on every incoming edge: otherwise the optimiser
-  // merges the loads into one at the loop top, which undoes the prefetch.
-  // (It waits for the first tile(s), which are needed next anyway.)
+  KVTile<TC> ta, tb;
+  load_tile<BS, TC>(ta, t0, c);
+  // The first tile passes through an empty asm so that ta is not a load on
+  // both incoming edges of the loop: otherwise the optimiser merges the two
+  // loads of ta into one at the loop top, which undoes the prefetch.
 #pragma unroll
   for (int ch = 0; ch < TC; ++ch)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      asm volatile("" : "+v"(cur.k[ch][s]), "+v"(cur.v[ch][s]));
-#if PKV_PREFETCH_TILES >= 2
-      asm volatile("" : "+v"(n1.k[ch][s]), "+v"(n1.v[ch][s]));
-#endif
-    }
+    for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(ta.k[ch][s]), "+v"(ta.v[ch][s]));
   while (true) {
-    KVTile<TC> nxt;
-    load_tile<BS, TC>(nxt, t0 + PKV_PREFETCH_TILES * TILE, c);
-    compute_tile<TC>(cur, t0, c.end, qop, a.scale_log2e, c, st);
+    load_tile<BS, TC>(tb, t0 + TILE, c);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_tile<TC>(ta, t0, c.end, qop, a.scale_log2e, c, st);
     t0 += TILE;
     if (t0 >= c.end) break;
-#if PKV_PREFETCH_TILES >= 2
-    cur = n1;
-    n1 = nxt;
-#else
-    cur = nxt;
-#endif
+    load_tile<BS, TC>(ta, t0 + TILE, c);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_tile<TC>(tb, t0, c.end, qop, a.scale_log2e, c, st);
+    t0 += TILE;
+    if (t0 >= c.end) break;
   }
 }
 

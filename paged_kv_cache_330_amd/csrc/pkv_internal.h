@@ -25,9 +25,6 @@ constexpr int kMaxBalancedSeqs = 2048;     // batch limit of the balanced schedu
 #ifndef PKV_MFMA_TILE_CHUNKS
 #define PKV_MFMA_TILE_CHUNKS 1  // 16-token chunks per wave tile
 #endif
-#ifndef PKV_PREFETCH_TILES
-#define PKV_PREFETCH_TILES 1    // tiles a wave has in flight ahead of the one it computes (1 or 2)
-#endif
 #ifndef PKV_KV_NONTEMPORAL
 #define PKV_KV_NONTEMPORAL 1    // K/V loads carry the streaming hint (0: plain loads)
 #endif
