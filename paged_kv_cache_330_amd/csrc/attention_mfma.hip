@@ -123,8 +123,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) PKV_BALANCED_OCCUPANCY void decode_
   const int per = max(1, (total + S - 1) / S);
 
   if (slice == 0)  // sequences of length 0 get zero rows
-    for (int j = 0; j < B; ++j)
-      if (s_cc[j + 1] == s_cc[j]) zero_rows<G>(a, j, kvh);
+    zero_rows_where<G>(a, B, kvh, [&](int j) { return s_cc[j + 1] == s_cc[j]; });
 
   const int c_lo = slice * per;
   const int c_hi = min(total, c_lo + per);

@@ -252,8 +252,9 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_shared_kernel(SharedArg
     }
   }
   if (slice == 0)  // sequences with no token at all get zero rows
-    for (int j = 0; j < B; ++j)
-      if (s_tail[j] == 0 && s_cc[NPS + j + 1] == s_cc[NPS + j]) zero_rows<G>(a, j, kvh);
+    zero_rows_where<G>(a, B, kvh, [&](int j) {
+      return s_tail[j] == 0 && s_cc[NPS + j + 1] == s_cc[NPS + j];
+    });
 
   // 7. This slice's chunks.
   const int c_lo = slice * per;

@@ -563,5 +563,22 @@ __device__ __forceinline__ void zero_rows(const DecodeArgs& a, int b, int kvh) {
   for (int i = lane; i < G * kD; i += 64) store_out(a, o + i, 0.f);
 }
 
+// Zero output rows (kv head kvh, one wave) of every sequence b < B for which
+// empty(b) holds.  The wave tests 64 sequences at a time and walks the ballot,
+// so the cost grows with the number of empty sequences, not with B.
+template <int G, class F>
+__device__ __forceinline__ void zero_rows_where(const DecodeArgs& a, int B, int kvh, F&& empty) {
+  const int lane = threadIdx.x & 63;
+  for (int base = 0; base < B; base += 64) {
+    const int j = base + lane;
+    unsigned long long m = __ballot(j < B && empty(j));
+    while (m) {
+      const int k = __builtin_ctzll(m);
+      m &= m - 1;
+      zero_rows<G>(a, base + k, kvh);
+    }
+  }
+}
+
 }  // namespace
 }  // namespace pkv
