@@ -104,6 +104,52 @@ def read_probe(torch):
     print(json.dumps({"read_probe_bytes": buf.numel(), "gbps_by_workgroups": res,
                       "best_gbps": max(res.values()),
                       "best_frac_of_peak": round(max(res.values()) / HBM_PEAK_GBPS, 4)}), flush=True)
+    del buf
+    torch.cuda.empty_cache()
+    paged_read_probe(torch, lib, sink, stream)
+
+
+def paged_read_probe(torch, lib, sink, stream):
+    """The metric workload's K/V blocks, read in block-table order with the
+    decode kernels' wave layout and no compute: what the decode could reach
+    if its compute and bookkeeping cost nothing."""
+    import ctypes
+    import numpy as np
+    from paged_kv_cache_330_amd.workloads import empty_device_caches, make_decode_workload
+    lib.pkv_probe_paged_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    w = make_decode_workload(3)
+    bs, hkv = w.block_size, w.num_kv_heads
+    order = np.concatenate([w.block_tables[b, :-(-int(L) // bs)]
+                            for b, L in enumerate(w.seq_lens)]).astype(np.int32)
+    assert order.min() >= 0 and order.max() < w.num_blocks
+    ids = torch.from_numpy(order).cuda()
+    pools = []
+    for _ in range(2):
+        kc, vc = empty_device_caches(w.num_blocks, bs, hkv, w.head_dim, "bf16", "cuda", fill="zero")
+        kc.normal_()
+        vc.normal_()
+        pools.append((kc, vc))
+    nbytes = len(order) * bs * hkv * w.head_dim * 2 * 2
+    res = {}
+    for wgs in (256, 512, 1024):
+        ts = []
+        for i in range(12):
+            kc, vc = pools[i % 2]
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if lib.pkv_probe_paged_read(ctypes.c_void_p(kc.data_ptr()), ctypes.c_void_p(vc.data_ptr()),
+                                        ctypes.c_void_p(ids.data_ptr()), len(order), bs, hkv,
+                                        ctypes.c_void_p(sink.data_ptr()), wgs, stream) != 0:
+                raise RuntimeError("paged read probe launch failed")
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        res[wgs] = round(nbytes / (statistics.median(ts[2:]) * 1e-3) / 1e9, 1)
+    print(json.dumps({"paged_read_probe": w.name, "blocks": len(order), "bytes": nbytes,
+                      "gbps_by_workgroups": res, "best_gbps": max(res.values()),
+                      "best_frac_of_peak": round(max(res.values()) / HBM_PEAK_GBPS, 4)}), flush=True)
 
 
 def counter_pass(torch, args):
