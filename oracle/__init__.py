@@ -10,6 +10,7 @@ from .pagedkv_oracle import (  # noqa: F401
     copy_ref,
     decode_ref,
     gather_sequence,
+    prefill_ref,
     softmax_attention,
     splitk_ref,
     transfer_ref,

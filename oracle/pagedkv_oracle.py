@@ -50,6 +50,7 @@ __all__ = [
     "gather_sequence",
     "softmax_attention",
     "decode_ref",
+    "prefill_ref",
     "contiguous_ref",
     "brute_ref",
     "splitk_ref",
@@ -177,6 +178,43 @@ def decode_ref(q, k_cache, v_cache, block_tables, seq_lens, scale, dtype: str) -
         for h in range(Hq):
             kvh = h // group
             out[b, h] = softmax_attention(qf[b, h], K[:, kvh], V[:, kvh], scale)
+    return out
+
+
+def prefill_ref(q, query_start, k_cache, v_cache, block_tables, seq_lens, scale,
+                dtype: str) -> np.ndarray:
+    """Paged attention of a prompt (or a chunk of one) over the cache, fp64 ``[T, Hq, D]``.
+
+    "Paged KV", "运行阶段": at prefill a sequence takes blocks in order and its
+    K/V are filled in, so the prompt's tokens are in the cache (the write is
+    ``write_ref``) before they attend.  Sequence ``b`` owns query rows
+    ``query_start[b] .. query_start[b + 1] - 1``: its ``n_b`` newest tokens, at
+    positions ``seq_lens[b] - n_b .. seq_lens[b] - 1`` (earlier tokens, if any,
+    are context already cached).  The token at position ``p`` attends to the
+    cached tokens ``0 .. p``, itself included and nothing after it: the decode
+    step is the case ``n_b = 1``.  Attention itself is ``softmax_attention``
+    with the consecutive head grouping of ``decode_ref``.
+    """
+    T, Hq, D = q.shape
+    Hkv = k_cache.shape[2]
+    if Hq % Hkv:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    group = Hq // Hkv
+    qf = widen(q, dtype)
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    for b in range(len(seq_lens)):
+        r0, r1 = int(query_start[b]), int(query_start[b + 1])
+        L, n = int(seq_lens[b]), r1 - r0
+        if n > L:
+            raise ValueError(f"sequence {b} has {n} new tokens but only {L} cached")
+        K = widen(gather_sequence(k_cache, block_tables[b], L), dtype)
+        V = widen(gather_sequence(v_cache, block_tables[b], L), dtype)
+        for i in range(n):
+            p = L - n + i
+            for h in range(Hq):
+                kvh = h // group
+                out[r0 + i, h] = softmax_attention(qf[r0 + i, h], K[:p + 1, kvh], V[:p + 1, kvh],
+                                                   scale)
     return out
 
 

@@ -419,3 +419,183 @@ def test_transfer_ref_moves_whole_blocks_between_pools():
     dev_v[1] = 0
     oracle.transfer_ref(dev_k, dev_v, host_k, host_v, [[0, 4], [2, 1]])   # swap back in
     assert np.array_equal(dev_k, before_k) and np.array_equal(dev_v, before_v)
+
+
+# --------------------------------------------------------------------------- prefill
+def load_golden_prefill(golden_dir):
+    with open(os.path.join(golden_dir, "prefill_hand.json")) as f:
+        g = json.load(f)
+    bs, nb, hkv, d = g["block_size"], g["num_blocks"], g["num_kv_heads"], g["head_dim"]
+    kc = np.full((nb, bs, hkv, d), np.nan)
+    vc = np.full((nb, bs, hkv, d), np.nan)
+    for t, (k, v) in enumerate(zip(g["k_tokens"], g["v_tokens"])):
+        blk = g["block_table"][t // bs]
+        kc[blk, t % bs, 0] = k
+        vc[blk, t % bs, 0] = v
+    q = np.array(g["q"], dtype=np.float64)
+    return (g, q, np.array(g["query_start"]), kc, vc, np.array([g["block_table"]]),
+            np.array([g["seq_len"]]))
+
+
+def _random_prefill_case(rng, lens, news, bs=4, hq=4, hkv=2, d=8):
+    """Random f32 pool; sequence b has lens[b] cached tokens, the last news[b] new."""
+    nb = sum(-(-L // bs) for L in lens) + 3
+    kc = rng.standard_normal((nb, bs, hkv, d)).astype(np.float32)
+    vc = rng.standard_normal((nb, bs, hkv, d)).astype(np.float32)
+    perm = rng.permutation(nb)
+    tables, pos = [], 0
+    width = max(-(-L // bs) for L in lens)
+    for L in lens:
+        n = -(-L // bs)
+        tables.append(list(perm[pos:pos + n]) + [0] * (width - n))
+        pos += n
+    qs = np.concatenate([[0], np.cumsum(news)]).astype(np.int64)
+    q = rng.standard_normal((int(qs[-1]), hq, d)).astype(np.float32)
+    return q, qs, kc, vc, np.array(tables, dtype=np.int64), np.array(lens)
+
+
+def _brute_prefill(q, qs, kc, vc, bt, lens, scale):
+    """Causal paged attention in pure-Python loops: token at position p sees 0..p."""
+    T, hq, d = q.shape
+    bs, hkv = kc.shape[1], kc.shape[2]
+    out = np.zeros((T, hq, d))
+    for b in range(len(lens)):
+        n = int(qs[b + 1] - qs[b])
+        for i in range(n):
+            p = int(lens[b]) - n + i
+            for h in range(hq):
+                kv = h // (hq // hkv)
+                sc, rows = [], []
+                for t in range(p + 1):
+                    blk, off = int(bt[b][t // bs]), t % bs
+                    sc.append(float(scale) * math.fsum(float(a) * float(c) for a, c in
+                                                       zip(q[qs[b] + i, h], kc[blk, off, kv])))
+                    rows.append([float(x) for x in vc[blk, off, kv]])
+                m = max(sc)
+                w = [math.exp(x - m) for x in sc]
+                den = math.fsum(w)
+                for j in range(d):
+                    out[qs[b] + i, h, j] = math.fsum(w[t] * rows[t][j] for t in range(p + 1)) / den
+    return out
+
+
+def pin_prefill_golden(fn, golden_dir):
+    g, q, qs, kc, vc, bt, lens = load_golden_prefill(golden_dir)
+    out = fn(q, qs, kc, vc, bt, lens, g["scale"], "f64")
+    return np.abs(out - np.array(g["expected_out"])).max() <= g["tolerance"]
+
+
+def pin_prefill_brute(fn):
+    rng = np.random.default_rng(21)
+    q, qs, kc, vc, bt, lens = _random_prefill_case(rng, [9, 5, 13], [4, 5, 1])
+    out = fn(q, qs, kc, vc, bt, lens, 0.35, "f32")
+    return np.abs(out - _brute_prefill(q, qs, kc, vc, bt, lens, 0.35)).max() <= 1e-12
+
+
+def pin_prefill_decode(fn):
+    # one new token per sequence is the decode step
+    rng = np.random.default_rng(22)
+    q, qs, kc, vc, bt, lens = _random_prefill_case(rng, [7, 1, 12], [1, 1, 1])
+    out = fn(q, qs, kc, vc, bt, lens, 0.5, "f32")
+    ref = oracle.decode_ref(q, kc, vc, bt, lens, 0.5, "f32")
+    return np.abs(out - ref).max() <= 1e-12
+
+
+def test_golden_prefill_hand(golden_dir):
+    assert pin_prefill_golden(oracle.prefill_ref, golden_dir)
+
+
+def test_prefill_matches_brute_force():
+    assert pin_prefill_brute(oracle.prefill_ref)
+
+
+def test_prefill_of_one_new_token_is_decode():
+    assert pin_prefill_decode(oracle.prefill_ref)
+
+
+def test_prefill_first_prompt_token_is_its_value_row():
+    # a fresh prompt (no context): token 0 attends to itself only
+    rng = np.random.default_rng(23)
+    q, qs, kc, vc, bt, lens = _random_prefill_case(rng, [6, 3], [6, 3])
+    out = oracle.prefill_ref(q, qs, kc, vc, bt, lens, 0.7, "f32")
+    for b in range(2):
+        v0 = oracle.widen(oracle.gather_sequence(vc, bt[b], 1), "f32")[0]
+        for h in range(4):
+            assert np.array_equal(out[qs[b], h], v0[h // 2])
+
+
+def test_prefill_is_causal():
+    # changing a token after position p leaves p's output alone; changing one
+    # at or before p changes it
+    rng = np.random.default_rng(24)
+    q, qs, kc, vc, bt, lens = _random_prefill_case(rng, [11], [6], bs=4)
+    base = oracle.prefill_ref(q, qs, kc, vc, bt, lens, 0.4, "f32")
+    p_row, p = 2, 11 - 6 + 2                      # row 2 is position 7
+    for t, changes in ((8, False), (10, False), (7, True), (0, True)):
+        k2 = kc.copy()
+        k2[bt[0][t // 4], t % 4] += 1.0
+        out = oracle.prefill_ref(q, qs, k2, vc, bt, lens, 0.4, "f32")
+        assert (not np.array_equal(out[p_row], base[p_row])) == changes, (t, p)
+
+
+def test_prefill_in_chunks_equals_whole_prompt():
+    # prefill of a 10-token prompt at once equals a 4-token chunk followed by a
+    # 6-token chunk whose first 4 tokens are context
+    rng = np.random.default_rng(25)
+    q, qs, kc, vc, bt, lens = _random_prefill_case(rng, [10], [10])
+    whole = oracle.prefill_ref(q, qs, kc, vc, bt, lens, 0.3, "f32")
+    first = oracle.prefill_ref(q[:4], np.array([0, 4]), kc, vc, bt, np.array([4]), 0.3, "f32")
+    second = oracle.prefill_ref(q[4:], np.array([0, 6]), kc, vc, bt, np.array([10]), 0.3, "f32")
+    assert np.array_equal(np.concatenate([first, second]), whole)
+
+
+def _prefill_variant(q, qs, kc, vc, bt, lens, scale, dtype, *, base=None, limit=None,
+                     row=None, kv_map=None):
+    """A copy of prefill_ref whose steps can be swapped for wrong ones."""
+    T, hq, d = q.shape
+    hkv = kc.shape[2]
+    group = hq // hkv
+    base = base or (lambda L, n: L - n)
+    limit = limit or (lambda p: p + 1)
+    row = row or (lambda r0, i: r0 + i)
+    kv_map = kv_map or (lambda h: h // group)
+    qf = po.widen(q, dtype)
+    out = np.zeros((T, hq, d))
+    for b in range(len(lens)):
+        r0, n, L = int(qs[b]), int(qs[b + 1] - qs[b]), int(lens[b])
+        K = po.widen(po.gather_sequence(kc, bt[b], L), dtype)
+        V = po.widen(po.gather_sequence(vc, bt[b], L), dtype)
+        for i in range(n):
+            p = base(L, n) + i
+            lim = min(L, limit(p))
+            for h in range(hq):
+                out[r0 + i, h] = po.softmax_attention(qf[row(r0, i), h], K[:lim, kv_map(h) % hkv],
+                                                      V[:lim, kv_map(h) % hkv], scale)
+    return out
+
+
+PREFILL_MUTANTS = {
+    "positions ignore the context": dict(base=lambda L, n: 0),
+    "token does not see itself": dict(limit=lambda p: p),
+    "token sees the next token": dict(limit=lambda p: p + 2),
+    "query row ignores query_start": dict(row=lambda r0, i: i),
+    "kv head = h % Hkv": dict(kv_map=lambda h: h),
+}
+
+
+def _prefill_pins(fn, golden_dir):
+    return {"golden": pin_prefill_golden(fn, golden_dir), "brute force": pin_prefill_brute(fn),
+            "decode": pin_prefill_decode(fn)}
+
+
+def test_unmutated_prefill_copy_passes_every_pin(golden_dir):
+    assert all(_prefill_pins(_prefill_variant, golden_dir).values())
+
+
+@pytest.mark.parametrize("name", sorted(PREFILL_MUTANTS))
+def test_each_planted_prefill_mistake_fails_a_pin(name, golden_dir):
+    def fn(*a):
+        return _prefill_variant(*a, **PREFILL_MUTANTS[name])
+    with np.errstate(all="ignore"):
+        res = _prefill_pins(fn, golden_dir)
+    assert not all(res.values()), f"mistake {name!r} passed every prefill pin: {res}"
