@@ -219,13 +219,45 @@ int pkv_attention_decode_shared(void* out, int32_t out_dtype, const void* q,
                                 int32_t num_groups, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/*
+ * Prefill attention over the paged pools ("Paged KV", section "运行阶段": at
+ * prefill a sequence takes blocks in order and its K/V are filled in, here by
+ * pkv_kv_write with one slot per prompt token; section "Attention Kernel 的
+ * 适配": K/V are read block by block through the block table).  Sequence b
+ * brings n_b = query_start[b + 1] - query_start[b] new tokens, its newest:
+ * positions seq_lens[b] - n_b .. seq_lens[b] - 1 (earlier tokens, if any, are
+ * cached context, so a long prompt can be processed in chunks).  For query
+ * head h of the new token at position p, kv = h / G:
+ *     out[row][h] = sum_{t <= p} softmax_t(scale * <q[row][h], K_t>) * V_t
+ * over the tokens t = 0 .. p reached through block_tables[b]; with n_b = 1
+ * this is the decode step.
+ *
+ *   out           [num_tokens][num_q_heads][head_dim], out_dtype, written;
+ *                 rows outside every sequence's range are not written.
+ *   q             [num_tokens][num_q_heads][head_dim], cache->dtype, read.
+ *   query_start   [num_seqs + 1] int32, nondecreasing, query_start[0] == 0,
+ *                 query_start[num_seqs] <= num_tokens; n_b <= seq_lens[b].
+ *                 A sequence whose range breaks this is skipped and flagged in
+ *                 the device error word.
+ *   block_tables, seq_lens, scale: as for pkv_attention_decode (seq_lens
+ *                 counts the new tokens too).
+ * The pools must be PKV_BF16 with head_dim 128, and num_seqs <= 2048.  No
+ * workspace.  num_seqs == 0 or num_tokens == 0 is a no-op.
+ */
+int pkv_attention_prefill(void* out, int32_t out_dtype, const void* q, int64_t num_tokens,
+                          const int32_t* query_start, const void* k_cache, const void* v_cache,
+                          const pkv_cache_desc* cache, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                          int32_t num_q_heads, float scale, void* stream);
+
 /* Message for the last non-OK return on this thread ("" if none). */
 const char* pkv_last_error(void);
 
 /*
  * Synchronises `stream`, then reads and clears the current device's error
  * word.  Returns PKV_OK if no kernel recorded a bad slot, block id, sequence
- * length, copy pair or shared-prefix description since the last check;
+ * length, copy pair, shared-prefix description or prefill query range since the
+ * last check;
  * otherwise PKV_ERR_INVALID_ARG with the offending kinds in pkv_last_error().
  */
 int pkv_check_device_errors(void* stream);

@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
 PROBE_LIB = os.path.join(PKG, "libpkv_probe.so")  # measurement support for bench.py
 SOURCES = ["api.hip", "kv_write.hip", "block_copy.hip", "attention_mfma.hip", "attention_valu.hip",
-           "attention_shared.hip"]
+           "attention_shared.hip", "attention_prefill.hip"]
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
 

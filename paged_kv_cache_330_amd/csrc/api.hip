@@ -434,6 +434,35 @@ int pkv_attention_decode_shared(void* out, int32_t out_dtype, const void* q, con
   return e == hipSuccess ? PKV_OK : hip_fail(e, "attention_decode_shared launch");
 }
 
+int pkv_attention_prefill(void* out, int32_t out_dtype, const void* q, int64_t num_tokens,
+                          const int32_t* query_start, const void* k_cache, const void* v_cache,
+                          const pkv_cache_desc* cache, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                          int32_t num_q_heads, float scale, void* stream) {
+  g_last_error.clear();
+  Plan base;
+  PKV_TRY(make_plan(cache, num_seqs, num_q_heads, max_blocks_per_seq, 0, &base));
+  PKV_TRY(check_decode_scalars(cache, num_q_heads, out_dtype, scale));
+  if (cache->dtype != PKV_BF16 || cache->head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "prefill attention needs bf16 pools with head_dim 128");
+  if (num_seqs > pkv::kMaxBalancedSeqs)
+    return fail(PKV_ERR_UNSUPPORTED, "prefill attention takes at most %d sequences, got %d",
+                pkv::kMaxBalancedSeqs, num_seqs);
+  if (num_tokens < 0 || num_tokens > 0x7FFFFFFF)
+    return fail(PKV_ERR_INVALID_ARG, "num_tokens %lld out of range", (long long)num_tokens);
+  if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
+  pkv::PrefillArgs pa{};
+  PKV_TRY(fill_decode_args(out, out_dtype, q, k_cache, v_cache, cache, block_tables,
+                           max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, scale, &pa.d));
+  PKV_TRY(check_ptr(query_start, 4, "query_start"));
+  PKV_TRY(error_word(&pa.d.err));
+  pa.query_start = query_start;
+  pa.num_tokens = num_tokens;
+  hipError_t e = pkv::launch_prefill(pa, cache->block_size, num_q_heads / cache->num_kv_heads,
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "attention_prefill launch");
+}
+
 int pkv_check_device_errors(void* stream) {
   g_last_error.clear();
   unsigned* err = nullptr;
@@ -447,12 +476,13 @@ int pkv_check_device_errors(void* stream) {
   const unsigned zero = 0;
   e = hipMemcpy(err, &zero, sizeof(zero), hipMemcpyHostToDevice);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpy(clear error word)");
-  return fail(PKV_ERR_INVALID_ARG, "device range checks failed:%s%s%s%s%s",
+  return fail(PKV_ERR_INVALID_ARG, "device range checks failed:%s%s%s%s%s%s",
               (word & pkv::kErrSlot) ? " slot>=num_blocks*block_size" : "",
               (word & pkv::kErrBlockId) ? " block_id_out_of_range" : "",
               (word & pkv::kErrSeqLen) ? " seq_len_out_of_range" : "",
               (word & pkv::kErrCopyPair) ? " copy_pair_out_of_range" : "",
-              (word & pkv::kErrShared) ? " shared_prefix_inconsistent" : "");
+              (word & pkv::kErrShared) ? " shared_prefix_inconsistent" : "",
+              (word & pkv::kErrQuery) ? " prefill_query_range_inconsistent" : "");
 }
 
 }  // extern "C"

@@ -54,48 +54,6 @@ constexpr int kMembers = kCols / G;                          // sequences per pr
 constexpr int kMaxPrefixStreams = kMaxBalancedSeqs + kMaxBalancedSeqs / kMembers<8>;
 constexpr int kMaxStreams = kMaxPrefixStreams + kMaxBalancedSeqs;
 
-// Exclusive prefix sums out[i] = count(0) + ... + count(i - 1) for i <= n of a
-// count that every thread can evaluate; returns out[n].  All threads of the
-// workgroup call it; it ends with a barrier.
-template <class F>
-__device__ __forceinline__ int block_scan(int n, int* out, int* s_wsum, F&& count) {
-  const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  int carry = 0;
-  for (int base = 0; base < n; base += blockDim.x) {
-    const int j = base + threadIdx.x;
-    const int cnt = j < n ? count(j) : 0;
-    int x = cnt;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(x, off);
-      if (lane >= off) x += y;
-    }
-    if (lane == 63) s_wsum[wave] = x;
-    __syncthreads();
-    int before = carry, total = 0;
-    for (int w = 0; w < nw; ++w) {
-      if (w < wave) before += s_wsum[w];
-      total += s_wsum[w];
-    }
-    if (j < n) out[j] = before + x - cnt;
-    carry += total;
-    __syncthreads();  // s_wsum is rewritten by the next round
-  }
-  if (threadIdx.x == 0) out[n] = carry;
-  __syncthreads();
-  return carry;
-}
-
-// Largest i in [0, n) with arr[i] <= v, for a nondecreasing arr with arr[0] <= v.
-__device__ __forceinline__ int last_at_most(const int* arr, int n, int v) {
-  int lo = 0, hi = n;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (arr[mid] <= v) lo = mid; else hi = mid;
-  }
-  return lo;
-}
-
 // Writes the partial results of a prefix piece: stream column cw = 16 n + col
 // goes to row row0 + cw when cw < ncols (the columns of existing members).
 template <int NS>

@@ -194,14 +194,29 @@ struct ValuState {
 template <int G>
 using WaveState = std::conditional_t<kPvOnMfma<G>, MfmaState<1>, ValuState<G>>;
 
+// Which tokens of a window a query column attends to.  WindowTokens: all of
+// them (decode).  CausalTokens: column set n of this lane stops below
+// limit[n] (prefill: a token sees the tokens up to its own position).
+struct WindowTokens {
+  __device__ __forceinline__ bool valid(int, int tok, int end) const { return tok < end; }
+};
+template <int NS>
+struct CausalTokens {
+  int limit[NS];
+  __device__ __forceinline__ bool valid(int n, int tok, int end) const {
+    return tok < end && tok < limit[n];
+  }
+};
+
 // Q.K^T of one loaded tile for NS sets of query columns, scaled by
-// scale * log2(e); tokens at or past `end` score -inf.  mt[n] is the tile's
-// maximum of set n over each column (all four row groups).
-template <int TC, int NS>
+// scale * log2(e); tokens the columns do not attend to (at or past `end`, or
+// past a column's limit) score -inf.  mt[n] is the tile's maximum of set n
+// over each column (all four row groups).
+template <int TC, int NS, class Lim = WindowTokens>
 __device__ __forceinline__ void tile_scores(const KVTile<TC>& r, int t0, int end,
                                             const bf16x8_t (&qop)[NS][4], float scale_log2e,
                                             const TileCtx& ctx, float (&x)[NS][TC][4],
-                                            float (&mt)[NS]) {
+                                            float (&mt)[NS], const Lim& lim = Lim{}) {
   const int qr = ctx.qr;
 #pragma unroll
   for (int n = 0; n < NS; ++n) mt[n] = -INFINITY;
@@ -228,7 +243,7 @@ __device__ __forceinline__ void tile_scores(const KVTile<TC>& r, int t0, int end
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = t0 + 16 * c + 4 * qr + i;
-        x[n][c][i] = tok < end ? sacc[i] * scale_log2e : -INFINITY;
+        x[n][c][i] = lim.valid(n, tok, end) ? sacc[i] * scale_log2e : -INFINITY;
         mt[n] = fmaxf(mt[n], x[n][c][i]);
       }
     }
@@ -262,13 +277,14 @@ __device__ __forceinline__ float softmax_update(float (&x)[TC][4], float mt, flo
 
 // Scores, online-softmax update and P.V accumulation for one loaded tile,
 // P.V on the matrix cores.
-template <int TC, int NS>
+template <int TC, int NS, class Lim = WindowTokens>
 __device__ __forceinline__ void compute_tile(const KVTile<TC>& r, int t0, int end,
                                              const bf16x8_t (&qop)[NS][4], float scale_log2e,
-                                             const TileCtx& ctx, MfmaState<NS>& st) {
+                                             const TileCtx& ctx, MfmaState<NS>& st,
+                                             const Lim& lim = Lim{}) {
   const int qr = ctx.qr;
   float x[NS][TC][4], mt[NS], alpha[NS];
-  tile_scores<TC, NS>(r, t0, end, qop, scale_log2e, ctx, x, mt);
+  tile_scores<TC, NS>(r, t0, end, qop, scale_log2e, ctx, x, mt, lim);
 #pragma unroll
   for (int n = 0; n < NS; ++n) alpha[n] = softmax_update<TC>(x[n], mt[n], st.m[n], st.l[n]);
   // out^T[d][col] += sum_t V[t][d] P[t][col] with v_mfma_f32_16x16x16_bf16, 16
@@ -322,7 +338,8 @@ __device__ __forceinline__ void compute_tile(const KVTile<TC>& r, int t0, int en
 template <int TC, int G>
 __device__ __forceinline__ void compute_tile(const KVTile<TC>& r, int t0, int end,
                                              const bf16x8_t (&qop)[1][4], float scale_log2e,
-                                             const TileCtx& ctx, ValuState<G>& st) {
+                                             const TileCtx& ctx, ValuState<G>& st,
+                                             const WindowTokens& = WindowTokens{}) {
   float x[1][TC][4], mt[1];
   tile_scores<TC, 1>(r, t0, end, qop, scale_log2e, ctx, x, mt);
   const float alpha = softmax_update<TC>(x[0], mt[0], st.m[0], st.l[0]);
@@ -371,9 +388,10 @@ __device__ __forceinline__ void load_query(const DecodeArgs& a, int b, int kvh, 
 // makes the wave wait for those loads at the end of every iteration.  The
 // scheduling barriers keep the loads ahead of the compute.  Past the window's
 // end the loads re-read its last chunk (or the query row) and are never used.
-template <int BS, int TC, int NS, class State>
+template <int BS, int TC, int NS, class State, class Lim = WindowTokens>
 __device__ __forceinline__ void stream_window(const DecodeArgs& a, const TileCtx& c, int begin,
-                                              const bf16x8_t (&qop)[NS][4], State& st) {
+                                              const bf16x8_t (&qop)[NS][4], State& st,
+                                              const Lim& lim = Lim{}) {
   constexpr int TILE = 16 * TC;
   int t0 = begin;
   KVTile<TC> ta, tb;
@@ -388,12 +406,12 @@ __device__ __forceinline__ void stream_window(const DecodeArgs& a, const TileCtx
   while (true) {
     load_tile<BS, TC>(tb, t0 + TILE, c);
     __builtin_amdgcn_sched_barrier(0);
-    compute_tile<TC>(ta, t0, c.end, qop, a.scale_log2e, c, st);
+    compute_tile<TC>(ta, t0, c.end, qop, a.scale_log2e, c, st, lim);
     t0 += TILE;
     if (t0 >= c.end) break;
     load_tile<BS, TC>(ta, t0 + TILE, c);
     __builtin_amdgcn_sched_barrier(0);
-    compute_tile<TC>(tb, t0, c.end, qop, a.scale_log2e, c, st);
+    compute_tile<TC>(tb, t0, c.end, qop, a.scale_log2e, c, st, lim);
     t0 += TILE;
     if (t0 >= c.end) break;
   }
@@ -413,12 +431,13 @@ struct TableCheck {
 // all waves.  `qrow` is a 256-byte row of this wave's queries: the target of
 // the prefetch past the end, which is never used.  Every thread of the
 // workgroup calls this with the same range.
-template <int BS, int TC, bool kCheck, int NS, class State>
+template <int BS, int TC, bool kCheck, int NS, class State, class Lim = WindowTokens>
 __device__ __forceinline__ void attend_table(const DecodeArgs& a, int* s_bt, u32x4_t* k_lds,
                                              u32x4_t* v_lds, const int32_t* bt,
                                              const uint16_t* qrow, int kvh, int begin, int end,
                                              const bf16x8_t (&qop)[NS][4], State& st,
-                                             TableCheck chk = TableCheck{nullptr, 0}) {
+                                             TableCheck chk = TableCheck{nullptr, 0},
+                                             const Lim& lim = Lim{}) {
   const int lane = threadIdx.x & 63;
   TileCtx c;
   c.tok_stride = (int64_t)a.num_kv_heads * kD;
@@ -458,7 +477,7 @@ __device__ __forceinline__ void attend_table(const DecodeArgs& a, int* s_bt, u32
     c.blk0 = blk0;
     c.end = wend;
     c.last_chunk = ((wend - 1) >> 4) << 4;
-    stream_window<BS, TC>(a, c, w0, qop, st);
+    stream_window<BS, TC>(a, c, w0, qop, st, lim);
   }
 }
 
@@ -578,6 +597,48 @@ __device__ __forceinline__ void zero_rows_where(const DecodeArgs& a, int B, int 
       zero_rows<G>(a, base + k, kvh);
     }
   }
+}
+
+// Exclusive prefix sums out[i] = count(0) + ... + count(i - 1) for i <= n of a
+// count that every thread can evaluate; returns out[n].  All threads of the
+// workgroup call it; it ends with a barrier.
+template <class F>
+__device__ __forceinline__ int block_scan(int n, int* out, int* s_wsum, F&& count) {
+  const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int carry = 0;
+  for (int base = 0; base < n; base += blockDim.x) {
+    const int j = base + threadIdx.x;
+    const int cnt = j < n ? count(j) : 0;
+    int x = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) s_wsum[wave] = x;
+    __syncthreads();
+    int before = carry, total = 0;
+    for (int w = 0; w < nw; ++w) {
+      if (w < wave) before += s_wsum[w];
+      total += s_wsum[w];
+    }
+    if (j < n) out[j] = before + x - cnt;
+    carry += total;
+    __syncthreads();  // s_wsum is rewritten by the next round
+  }
+  if (threadIdx.x == 0) out[n] = carry;
+  __syncthreads();
+  return carry;
+}
+
+// Largest i in [0, n) with arr[i] <= v, for a nondecreasing arr with arr[0] <= v.
+__device__ __forceinline__ int last_at_most(const int* arr, int n, int v) {
+  int lo = 0, hi = n;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (arr[mid] <= v) lo = mid; else hi = mid;
+  }
+  return lo;
 }
 
 }  // namespace

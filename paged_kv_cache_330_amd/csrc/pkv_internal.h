@@ -15,6 +15,7 @@ enum : unsigned {
   kErrSeqLen = 4u,     // seq_len < 0 or > max_blocks_per_seq * block_size
   kErrCopyPair = 8u,   // copy src/dst outside [0, num_blocks)
   kErrShared = 16u,    // shared-prefix description disagrees with the tables or lengths
+  kErrQuery = 32u,     // prefill query range out of order, past num_tokens or longer than seq_len
 };
 
 constexpr int kDefaultPartitionTokens = 512;
@@ -143,5 +144,15 @@ struct SharedArgs {
 };
 
 hipError_t launch_shared_decode(const SharedArgs& a, int block_size, int group, hipStream_t stream);
+
+// Prefill attention (attention_prefill.hip): new tokens of sequence b are the
+// query rows query_start[b] .. query_start[b + 1] - 1 of d.q and d.out.
+struct PrefillArgs {
+  DecodeArgs d;                 // no workspace
+  const int32_t* query_start;   // [num_seqs + 1]
+  int64_t num_tokens;           // rows of q and out
+};
+
+hipError_t launch_prefill(const PrefillArgs& a, int block_size, int group, hipStream_t stream);
 
 }  // namespace pkv

@@ -26,6 +26,7 @@ __all__ = [
     "pkv_attention_decode",
     "pkv_attention_shared_workspace_bytes",
     "pkv_attention_decode_shared",
+    "pkv_attention_prefill",
     "pkv_check_device_errors",
     "pkv_last_error",
     "PKV_F32",
@@ -81,10 +82,13 @@ def load_library() -> ctypes.CDLL:
     lib.pkv_attention_shared_workspace_bytes.restype = SZ
     lib.pkv_attention_decode_shared.argtypes = [P, I32, P, P, P, D, P, I32, P, I32, I32,
                                                 ctypes.c_float, P, P, P, I32, P, SZ, P]
+    lib.pkv_attention_prefill.argtypes = [P, I32, P, I64, P, P, P, D, P, I32, P, I32, I32,
+                                          ctypes.c_float, P]
     lib.pkv_last_error.restype = ctypes.c_char_p
     lib.pkv_check_device_errors.argtypes = [P]
     for name in ("pkv_kv_write", "pkv_block_copy", "pkv_block_transfer", "pkv_attention_decode",
-                 "pkv_attention_decode_shared", "pkv_check_device_errors"):
+                 "pkv_attention_decode_shared", "pkv_attention_prefill",
+                 "pkv_check_device_errors"):
         getattr(lib, name).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -284,6 +288,36 @@ def pkv_attention_decode_shared(out: torch.Tensor, q: torch.Tensor, k_cache: tor
         _ptr(out), _DTYPES[out.dtype], _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
         _ptr(block_tables), mb, _ptr(seq_lens), B, Hq, float(scale), _ptr(group_offsets),
         _ptr(group_seqs), _ptr(group_lens), ng, _ptr(workspace), wbytes, _stream()))
+    return out
+
+
+def pkv_attention_prefill(out: torch.Tensor, q: torch.Tensor, query_start: torch.Tensor,
+                          k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                          scale: float) -> torch.Tensor:
+    """Causal attention of new tokens ``q`` ``[T, Hq, D]`` over the paged cache; returns ``out``.
+
+    ``query_start`` (int32 ``[B + 1]``) splits the rows of ``q``/``out`` by
+    sequence; the new tokens are each sequence's newest ``seq_lens`` positions.
+    """
+    desc = _desc(k_cache, v_cache)
+    _need(q, "q", dtype=k_cache.dtype, ndim=3)
+    _need(out, "out", ndim=3)
+    if out.dtype not in _DTYPES:
+        raise TypeError("out must be float32 or bfloat16")
+    _need(query_start, "query_start", dtype=torch.int32, ndim=1)
+    _need(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _need(seq_lens, "seq_lens", dtype=torch.int32, ndim=1)
+    T, Hq, D = q.shape
+    B = seq_lens.shape[0]
+    if tuple(out.shape) != (T, Hq, D) or D != desc.head_dim:
+        raise ValueError("out/q shapes do not match [T, Hq, head_dim]")
+    if block_tables.shape[0] != B or query_start.shape[0] != B + 1:
+        raise ValueError("block_tables must have B rows and query_start B + 1 entries")
+    _check(load_library().pkv_attention_prefill(
+        _ptr(out), _DTYPES[out.dtype], _ptr(q), T, _ptr(query_start), _ptr(k_cache), _ptr(v_cache),
+        ctypes.byref(desc), _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), B, Hq,
+        float(scale), _stream()))
     return out
 
 

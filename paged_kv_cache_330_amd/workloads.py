@@ -44,6 +44,7 @@ __all__ = [
     "DecodeWorkload",
     "make_decode_workload",
     "PrefixSharingWorkload",
+    "PrefillWorkload",
 ]
 
 
@@ -395,6 +396,63 @@ class PrefixSharingWorkload:
         shape = (self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim)
         val = 0x7FC0 if fill == "nan" else 0
         return np.full(shape, val, np.uint16), np.full(shape, val, np.uint16)
+
+
+class PrefillWorkload:
+    """Prompts (or prompt chunks after cached context) in a paged pool.
+
+    Sequence ``b`` holds ``context[b] + new[b]`` tokens, placed by a block
+    manager over a seeded free order ("Paged KV", "运行阶段": prefill takes
+    blocks in order).  All tokens' K/V are written with one slot mapping
+    (``slots``, rows of ``k_tokens``/``v_tokens`` in sequence order); the
+    ``new[b]`` newest tokens of each sequence are the query rows ``q`` split by
+    ``query_start``.  Values are standard normals rounded to bf16.
+    """
+
+    def __init__(self, context, new, block_size: int = 16, num_q_heads: int = 32,
+                 num_kv_heads: int = 8, head_dim: int = 128, seed: int = 7):
+        context, new = [int(c) for c in context], [int(n) for n in new]
+        if len(context) != len(new):
+            raise ValueError("context and new must have one entry per sequence")
+        self.block_size, self.head_dim = block_size, head_dim
+        self.num_q_heads, self.num_kv_heads = num_q_heads, num_kv_heads
+        self.dtype = "bf16"
+        self.scale = np.float32(1.0 / math.sqrt(head_dim))
+        self.num_seqs = len(new)
+        self.seq_lens = np.array([c + n for c, n in zip(context, new)], dtype=np.int32)
+        self.query_start = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+        self.num_tokens = int(self.query_start[-1])
+        rng = np.random.default_rng(seed)
+        need = sum(-(-int(L) // block_size) for L in self.seq_lens)
+        self.num_blocks = max(1, math.ceil(1.1 * need))
+        self.manager = BlockManager(self.num_blocks, block_size, rng.permutation(self.num_blocks))
+        slots = []
+        for b, L in enumerate(self.seq_lens):
+            self.manager.add_sequence(b)
+            s, _ = self.manager.append_tokens(b, int(L))
+            slots.extend(s)
+        self.slots = np.asarray(slots, dtype=np.int64)
+        total = int(self.seq_lens.sum())
+        Hkv, D = num_kv_heads, head_dim
+        self.k_tokens = _normal(rng, (total, Hkv, D), "bf16")
+        self.v_tokens = _normal(rng, (total, Hkv, D), "bf16")
+        self.q = _normal(rng, (self.num_tokens, num_q_heads, D), "bf16")
+        width = max(1, max(-(-int(L) // block_size) for L in self.seq_lens))
+        self.block_tables = self.manager.tables_array(list(range(self.num_seqs)), width=width)
+
+    def empty_caches(self, fill: str = "nan"):
+        shape = (self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim)
+        val = 0x7FC0 if fill == "nan" else 0
+        return np.full(shape, val, np.uint16), np.full(shape, val, np.uint16)
+
+    def flops(self) -> int:
+        """Multiply-adds x 2 of Q.K^T and P.V: 4 D Hq (p + 1) per new token at position p."""
+        total = 0
+        for b in range(self.num_seqs):
+            n = int(self.query_start[b + 1] - self.query_start[b])
+            L = int(self.seq_lens[b])
+            total += sum(L - n + i + 1 for i in range(n))
+        return 4 * self.head_dim * self.num_q_heads * total
 
 
 # ---------------------------------------------------------------------------- device upload

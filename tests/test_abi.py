@@ -256,3 +256,28 @@ def test_shared_prefix_validation(lib):
     assert shared(lib, ws=P(0)) == WORKSPACE
     need = shared_ws(lib, desc(), 32, 32, 4)
     assert shared(lib, wsb=need - 1) == WORKSPACE
+
+
+def prefill(lib, **kw):
+    a = dict(out=P(), out_dtype=0, q=P(), T=64, qs=P(), k=P(), v=P(), desc=desc(), bt=P(), mb=32,
+             sl=P(), B=4, Hq=32, scale=0.088)
+    a.update(kw)
+    return lib.pkv_attention_prefill(a["out"], a["out_dtype"], a["q"], a["T"], a["qs"], a["k"],
+                                     a["v"], ctypes.byref(a["desc"]), a["bt"], a["mb"], a["sl"],
+                                     a["B"], a["Hq"], a["scale"], P(0))
+
+
+def test_prefill_validation(lib):
+    assert prefill(lib, B=0, out=P(0), q=P(0)) == OK                # no-op
+    assert prefill(lib, T=0, out=P(0), q=P(0)) == OK                # no-op
+    assert prefill(lib, desc=desc(dtype=0)) == UNSUPPORTED
+    assert "bf16" in ops.pkv_last_error()
+    assert prefill(lib, desc=desc(d=64)) == UNSUPPORTED
+    assert prefill(lib, B=2049) == UNSUPPORTED
+    assert prefill(lib, Hq=24) == UNSUPPORTED                       # group 3
+    assert prefill(lib, T=-1) == INVALID
+    assert prefill(lib, qs=P(0)) == INVALID
+    assert prefill(lib, qs=P(FAKE + 2)) == INVALID
+    assert prefill(lib, q=P(FAKE + 8)) == INVALID
+    assert prefill(lib, scale=float("nan")) == INVALID
+    assert prefill(lib, mb=0) == INVALID
