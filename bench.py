@@ -59,6 +59,8 @@ def parse():
                    help="only time a plain streaming read of 4 GiB (context for the roofline)")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device copy (HBM counter calibration)")
+    p.add_argument("--prefill", action="store_true",
+                   help="only time paged prefill (prompt write + causal attention) workloads")
     p.add_argument("--counter-pass", action="store_true",
                    help="only run 4 decode calls of the workload (a 1 GiB write between calls "
                         "evicts the pool from the caches), then 3 streaming reads of 2 GiB: "
@@ -466,6 +468,7 @@ def swap_report(torch, ops, blocks=2048, reps=5):
 
 def report_all(torch, ops, args):
     """One JSON line per workload other than the metric's (shorter runs)."""
+    prefill_report(torch, ops)
     from paged_kv_cache_330_amd.workloads import PrefixSharingWorkload, make_decode_workload
     steps, warmup = 20, 3
     for config, bs in ((2, None), (4, 32), (4, 64)):
@@ -511,6 +514,68 @@ def report_all(torch, ops, args):
             torch.cuda.empty_cache()
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+PREFILL_WORKLOADS = [
+    # name, context tokens per sequence, new tokens per sequence, sequences
+    ("prefix_sharing_prompts", 0, 2044, 4),
+    ("llama3_8b_prompts_16x2048", 0, 2048, 16),
+    ("chunks_512_after_4096", 4096, 512, 8),
+]
+
+
+def prefill_report(torch, ops, reps=10):
+    """Paged prefill of Llama-3-8B-shaped prompts (32 q / 8 kv heads, head_dim
+    128, bf16, block size 16): the write of every prompt token through the
+    slot mapping, then causal attention of the new tokens.  The attention is
+    bound by the matrix cores: algorithmic flops = 4 D Hq (p + 1) per new
+    token at position p, against the dense bf16 MFMA peak."""
+    from paged_kv_cache_330_amd.workloads import (PrefillWorkload, empty_device_caches,
+                                                  torch_tensor)
+    dev = "cuda"
+    for name, ctx, new, nseq in PREFILL_WORKLOADS:
+        w = PrefillWorkload([ctx] * nseq, [new] * nseq, block_size=16, seed=13)
+        kc, vc = empty_device_caches(w.num_blocks, 16, w.num_kv_heads, w.head_dim, "bf16", dev,
+                                     fill="zero")
+        kt, vt = torch_tensor(w.k_tokens, "bf16", dev), torch_tensor(w.v_tokens, "bf16", dev)
+        slots = torch.from_numpy(w.slots).to(dev)
+        q = torch_tensor(w.q, "bf16", dev)
+        qs = torch.from_numpy(w.query_start).to(dev)
+        bt = torch.from_numpy(w.block_tables).to(dev)
+        sl = torch.from_numpy(w.seq_lens).to(dev)
+        out = torch.empty((w.num_tokens, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+        write = lambda: ops.pkv_kv_write(kt, vt, slots, kc, vc)  # noqa: E731
+        attend = lambda: ops.pkv_attention_prefill(out, q, qs, kc, vc, bt, sl, float(w.scale))  # noqa: E731
+        res = {"workload": name, "num_seqs": nseq, "context_tokens": ctx, "new_tokens": new,
+               "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+               "head_dim": w.head_dim, "block_size": 16}
+        for label, call in (("write", write), ("attn", attend)):
+            call()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                call()
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            ops.pkv_check_device_errors()
+            res[f"t_{label}_us"] = round(statistics.median(ts) * 1e3, 2)
+        row = w.num_kv_heads * w.head_dim * 2
+        wbytes = 2 * 2 * len(w.slots) * row + 8 * len(w.slots)
+        res["write_gbps"] = round(wbytes / (res["t_write_us"] * 1e-6) / 1e9, 1)
+        flops = w.flops()
+        tflops = flops / (res["t_attn_us"] * 1e-6) / 1e12
+        res["attn_flops"] = flops
+        res["attn_tflops"] = round(tflops, 1)
+        res["attn_mfma_frac"] = round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)
+        res["prompt_tokens_per_s"] = round(w.num_tokens / ((res["t_write_us"] + res["t_attn_us"]) * 1e-6), 1)
+        print(json.dumps({"report": res}), flush=True)
+        del kc, vc, kt, vt
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -533,6 +598,9 @@ def main():
     from paged_kv_cache_330_amd.workloads import make_decode_workload
 
     ops.load_library()
+    if args.prefill:
+        prefill_report(torch, ops)
+        return
     if args.report_all:
         report_all(torch, ops, args)
     t_gen = time.perf_counter()
