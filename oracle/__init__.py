@@ -9,11 +9,15 @@ from .pagedkv_oracle import (  # noqa: F401
     contiguous_ref,
     copy_ref,
     decode_ref,
+    dequantize_fp8,
+    e4m3_encode,
+    e4m3_value,
     gather_sequence,
     prefill_ref,
     softmax_attention,
     splitk_ref,
     transfer_ref,
     widen,
+    write_fp8_ref,
     write_ref,
 )

@@ -51,6 +51,10 @@ __all__ = [
     "softmax_attention",
     "decode_ref",
     "prefill_ref",
+    "e4m3_value",
+    "e4m3_encode",
+    "write_fp8_ref",
+    "dequantize_fp8",
     "contiguous_ref",
     "brute_ref",
     "splitk_ref",
@@ -216,6 +220,76 @@ def prefill_ref(q, query_start, k_cache, v_cache, block_tables, seq_lens, scale,
                 out[r0 + i, h] = softmax_attention(qf[r0 + i, h], K[:p + 1, kvh], V[:p + 1, kvh],
                                                    scale)
     return out
+
+
+# ---------------------------------------------------------------------------- FP8 KV
+# "Paged KV", section "局限性": some KV quantization schemes store FP8 with a
+# scale per block.  Read here as OCP FP8 E4M3 codes (1 sign, 4 exponent bits
+# with bias 7, 3 mantissa bits, no infinities, S.1111.111 = NaN, largest finite
+# 448) and one fp32 scale per (physical block, kv head), for K and for V: a
+# cached element is scale * value(code).
+
+def e4m3_value(code) -> np.ndarray:
+    """The real value of each E4M3 code (uint8), fp64; NaN for S.1111.111."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e.astype(np.float64) - 7))
+    mag = np.where((e == 15) & (c & 0x7 == 7), np.nan, mag)
+    return sign * mag
+
+
+_E4M3_POS = e4m3_value(np.arange(0x7F))          # codes 0x00 .. 0x7E, increasing
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest E4M3 code of each (exactly representable fp64) value, uint8.
+
+    Round to nearest, ties to the code with an even mantissa; magnitudes above
+    448 saturate to 448; NaN gives S.1111.111.  The nearest grid point is found
+    by search over the 127 non-negative finite values, not by bit arithmetic.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    mag = np.abs(x)
+    idx = np.searchsorted(_E4M3_POS, np.minimum(mag, 448.0))     # first grid value >= mag
+    hi = np.minimum(idx, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = mag - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[hi] - np.minimum(mag, 448.0)
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0) & (hi != lo))
+    code = np.where(mag >= 448.0, 0x7E, np.where(pick_hi, hi, lo)).astype(np.int64)
+    code = np.where(np.isnan(x), 0x7F, code)
+    code = code | np.where(np.signbit(x), 0x80, 0)
+    return code.astype(np.uint8)
+
+
+def write_fp8_ref(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale) -> None:
+    """Slot-mapping write into FP8 pools (uint8 codes), in place.
+
+    Each element x (bf16 bit patterns in ``k``/``v``) of kv head ``h`` of a
+    token whose slot lies in block ``blk`` becomes
+    ``e4m3_encode(fp32(x / scale[blk, h]))``: the quotient is the binary32
+    division of the two binary32 values, the same decision the device takes.
+    Negative slots are skipped, as by ``write_ref``.
+    """
+    bs = k_cache.shape[1]
+    kx = widen(k, "bf16").astype(np.float32)
+    vx = widen(v, "bf16").astype(np.float32)
+    ks = np.asarray(k_scale, dtype=np.float32)
+    vs = np.asarray(v_scale, dtype=np.float32)
+    for i, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64).tolist()):
+        if slot < 0:
+            continue
+        blk, off = slot // bs, slot % bs
+        k_cache[blk, off] = e4m3_encode((kx[i] / ks[blk][:, None]).astype(np.float64))
+        v_cache[blk, off] = e4m3_encode((vx[i] / vs[blk][:, None]).astype(np.float64))
+
+
+def dequantize_fp8(cache, scale) -> np.ndarray:
+    """FP8 pool (uint8 codes) -> fp64 values: scale[blk, h] * value(code)."""
+    s = np.asarray(scale, dtype=np.float32).astype(np.float64)
+    return e4m3_value(cache) * s[:, None, :, None]
 
 
 def contiguous_ref(q, k_seqs, v_seqs, scale, dtype: str) -> np.ndarray:

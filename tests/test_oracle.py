@@ -599,3 +599,90 @@ def test_each_planted_prefill_mistake_fails_a_pin(name, golden_dir):
     with np.errstate(all="ignore"):
         res = _prefill_pins(fn, golden_dir)
     assert not all(res.values()), f"mistake {name!r} passed every prefill pin: {res}"
+
+
+# --------------------------------------------------------------------------- FP8 E4M3 KV
+def _spec_value(code):
+    """OCP FP8 E4M3 written out per code in plain Python (bias 7, no infinities)."""
+    s = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 0x7
+    if e == 15 and m == 7:
+        return math.nan
+    if e == 0:
+        return s * math.ldexp(m, -9)
+    return s * math.ldexp(8 + m, e - 10)
+
+
+def _rne_bits(x32):
+    """E4M3 RNE of binary32 values by bit arithmetic on the binary32 word."""
+    u = np.asarray(x32, dtype=np.float32).view(np.uint32).astype(np.int64)
+    sign = (u >> 31) << 7
+    a = u & 0x7FFFFFFF
+    mag = np.abs(np.asarray(x32, dtype=np.float32).astype(np.float64))
+    q = a >> 20
+    rem = a & 0xFFFFF
+    q = q + ((rem > 0x80000) | ((rem == 0x80000) & (q & 1 == 1))).astype(np.int64)
+    normal = q - (120 << 3)
+    sub = np.rint(mag * 512.0).astype(np.int64)          # round half to even
+    code = np.where(mag < 2.0 ** -6, sub, normal)
+    code = np.where(mag >= 448.0, 0x7E, code)
+    code = np.where(a > 0x7F800000, 0x7F, code)
+    return (code | sign).astype(np.uint8)
+
+
+def test_e4m3_values_follow_the_format():
+    vals = oracle.e4m3_value(np.arange(256))
+    for c in range(256):
+        ref = _spec_value(c)
+        assert (math.isnan(ref) and math.isnan(vals[c])) or vals[c] == ref, c
+    assert vals[0x7E] == 448.0 and vals[0x08] == 2.0 ** -6 and vals[0x01] == 2.0 ** -9
+    assert np.isnan(vals[0x7F]) and np.isnan(vals[0xFF]) and np.signbit(vals[0x80])
+
+
+def test_e4m3_encode_round_trips_every_code():
+    codes = np.arange(256)
+    vals = oracle.e4m3_value(codes)
+    ok = ~np.isnan(vals)
+    assert np.array_equal(oracle.e4m3_encode(vals[ok]), codes[ok].astype(np.uint8))
+
+
+def test_e4m3_encode_ties_saturation_and_specials():
+    # (value, code): ties go to the even code, magnitudes past 448 saturate
+    cases = [(1.0625, 0x38), (1.1875, 0x3A), (1.9375, 0x40), (2.0 ** -10, 0x00),
+             (3 * 2.0 ** -10, 0x02), (448.0, 0x7E), (449.0, 0x7E), (464.0, 0x7E), (1e30, 0x7E),
+             (-500.0, 0xFE), (0.0, 0x00), (-0.0, 0x80), (240.0, 0x77), (232.0, 0x76)]
+    got = oracle.e4m3_encode(np.array([x for x, _ in cases]))
+    assert got.tolist() == [c for _, c in cases]
+    assert oracle.e4m3_encode([np.nan]).tolist() == [0x7F]
+
+
+def test_e4m3_encode_matches_bit_arithmetic_rne():
+    # the nearest-grid search and an RNE on the binary32 bits agree on random
+    # values over the whole range, on every midpoint between neighbours and on
+    # values one binary32 ulp either side of each midpoint
+    rng = np.random.default_rng(31)
+    x = (rng.standard_normal(1 << 20) * np.exp2(rng.uniform(-14, 10, 1 << 20))).astype(np.float32)
+    grid = oracle.e4m3_value(np.arange(0x7F))
+    mids = ((grid[:-1] + grid[1:]) / 2).astype(np.float32)
+    near = np.concatenate([mids, np.nextafter(mids, np.float32(np.inf)),
+                           np.nextafter(mids, np.float32(-np.inf))])
+    x = np.concatenate([x, near, -near])
+    assert np.array_equal(oracle.e4m3_encode(x.astype(np.float64)), _rne_bits(x))
+
+
+def test_write_fp8_ref_by_hand():
+    # bs 2, one kv head, head_dim 2.  Block 1 has K scale 0.5, V scale 2:
+    # K (1, -3) / 0.5 = (2, -6) -> 0x40, 0xCC;  V (3, 0.25) / 2 = (1.5, 0.125) -> 0x3C, 0x20
+    # (2 = 2^1: E 8, M 0; 6 = 1.5 2^2: E 9, M 4; 1.5: E 7, M 4; 0.125 = 2^-3: E 4, M 0).
+    kc = np.zeros((2, 2, 1, 2), np.uint8)
+    vc = np.zeros((2, 2, 1, 2), np.uint8)
+    k = bf16_round(np.array([[[1.0, -3.0]]], np.float32))
+    v = bf16_round(np.array([[[3.0, 0.25]]], np.float32))
+    ks = np.array([[1.0], [0.5]], np.float32)
+    vs = np.array([[1.0], [2.0]], np.float32)
+    oracle.write_fp8_ref(k, v, [3], kc, vc, ks, vs)      # slot 3: block 1, offset 1
+    assert kc[1, 1, 0].tolist() == [0x40, 0xCC] and vc[1, 1, 0].tolist() == [0x3C, 0x20]
+    assert not kc[0].any() and not kc[1, 0].any()
+    deq = oracle.dequantize_fp8(kc, ks)
+    assert deq[1, 1, 0].tolist() == [1.0, -3.0]
+    oracle.write_fp8_ref(k, v, [-1], kc, vc, ks, vs)     # skipped
