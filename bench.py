@@ -59,6 +59,8 @@ def parse():
                    help="only time a plain streaming read of 4 GiB (context for the roofline)")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device copy (HBM counter calibration)")
+    p.add_argument("--fp8", action="store_true",
+                   help="only the batch-256 GQA decode step over FP8 E4M3 pools")
     p.add_argument("--prefill", action="store_true",
                    help="only time paged prefill (prompt write + causal attention) workloads")
     p.add_argument("--counter-pass", action="store_true",
@@ -274,8 +276,9 @@ class Step:
     """Device tensors of one decode step and the phases that run it."""
 
     def __init__(self, torch, ops, pools, q, bt, sl, k_new, v_new, slots, pairs, scale,
-                 partition_tokens, groups=None):
+                 partition_tokens, groups=None, fp8_scales=None):
         self.torch, self.ops = torch, ops
+        self.fp8 = fp8_scales  # (k_scale, v_scale) device tensors: FP8 pools
         self.pools, self.q, self.bt, self.sl = pools, q, bt, sl
         self.k_new, self.v_new, self.slots, self.pairs = k_new, v_new, slots, pairs
         self.scale, self.part = scale, partition_tokens
@@ -294,6 +297,20 @@ class Step:
         kc, vc = self.pools[i % len(self.pools)]
         if ev:
             ev[0].record()
+        if self.fp8 is not None:
+            ks, vs = self.fp8
+            if self.pairs is not None:
+                self.ops.pkv_block_copy_fp8(kc, vc, ks, vs, self.pairs)
+            if ev:
+                ev[1].record()
+            self.ops.pkv_kv_write_fp8(self.k_new, self.v_new, self.slots, kc, vc, ks, vs)
+            if ev:
+                ev[2].record()
+            self.ops.pkv_attention_decode_fp8(self.out, self.q, kc, vc, ks, vs, self.bt, self.sl,
+                                              self.scale, self.part, self.ws)
+            if ev:
+                ev[3].record()
+            return
         if self.pairs is not None:
             self.ops.pkv_block_copy(kc, vc, self.pairs)
         if ev:
@@ -333,6 +350,34 @@ def decode_step_state(torch, ops, w, npools, partition_tokens):
                 torch.from_numpy(w.block_tables).to(dev), torch.from_numpy(w.seq_lens).to(dev),
                 k_new, v_new, torch.from_numpy(w.step_slots).to(dev), None, float(w.scale),
                 partition_tokens)
+
+
+def fp8_step_state(torch, ops, w, npools, partition_tokens):
+    """FP8 pools (E4M3 codes, max-abs block scales) holding the prefill of
+    decode workload `w`, and its step."""
+    from paged_kv_cache_330_amd.workloads import torch_tensor
+    dev = "cuda"
+    ks_h, vs_h = w.fp8_scales(unused=1.0)
+    ks, vs = torch.from_numpy(ks_h).to(dev), torch.from_numpy(vs_h).to(dev)
+    kt, vt = torch_tensor(w.k_tokens, "bf16", dev), torch_tensor(w.v_tokens, "bf16", dev)
+    pre = torch.from_numpy(w.prefill_rows).to(dev)
+    pre_slots = torch.from_numpy(w.prefill_slots).to(dev)
+    k_pre, v_pre = kt[pre].contiguous(), vt[pre].contiguous()
+    step = torch.from_numpy(w.step_rows).to(dev)
+    k_new, v_new = kt[step].contiguous(), vt[step].contiguous()
+    del kt, vt
+    shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
+    pools = []
+    for _ in range(npools):
+        kc = torch.zeros(shape, dtype=torch.uint8, device=dev)
+        vc = torch.zeros(shape, dtype=torch.uint8, device=dev)
+        ops.pkv_kv_write_fp8(k_pre, v_pre, pre_slots, kc, vc, ks, vs)
+        pools.append((kc, vc))
+    del k_pre, v_pre
+    return Step(torch, ops, pools, torch_tensor(w.q, "bf16", dev),
+                torch.from_numpy(w.block_tables).to(dev), torch.from_numpy(w.seq_lens).to(dev),
+                k_new, v_new, torch.from_numpy(w.step_slots).to(dev), None, float(w.scale),
+                partition_tokens, fp8_scales=(ks, vs))
 
 
 def sharing_step_state(torch, ops, ws, final, partition_tokens, shared=False):
@@ -393,6 +438,15 @@ def attn_bytes(seq_lens, B, Hq, Hkv, D, bs, es):
     kv = int(sum(int(L) for L in seq_lens)) * Hkv * D * 2 * es
     entries = int(sum(math.ceil(int(L) / bs) for L in seq_lens))
     return kv, kv + B * Hq * D * es + B * Hq * D * 4 + 4 * entries + 4 * B
+
+
+def attn_bytes_fp8(seq_lens, B, Hq, Hkv, D, bs):
+    """Algorithmic bytes of one FP8 decode call: 1-byte K/V codes, a K and a V
+    fp32 scale per (table entry, kv head), bf16 q, fp32 out, table entries,
+    lengths."""
+    kv = int(sum(int(L) for L in seq_lens)) * Hkv * D * 2
+    entries = int(sum(math.ceil(int(L) / bs) for L in seq_lens))
+    return kv, kv + 8 * entries * Hkv + B * Hq * D * 2 + B * Hq * D * 4 + 4 * entries + 4 * B
 
 
 def _pct(xs, p):
@@ -468,6 +522,7 @@ def swap_report(torch, ops, blocks=2048, reps=5):
 
 def report_all(torch, ops, args):
     """One JSON line per workload other than the metric's (shorter runs)."""
+    fp8_report(torch, ops, args)
     prefill_report(torch, ops)
     from paged_kv_cache_330_amd.workloads import PrefixSharingWorkload, make_decode_workload
     steps, warmup = 20, 3
@@ -512,6 +567,30 @@ def report_all(torch, ops, args):
             print(json.dumps({"report": res}), flush=True)
             del st
             torch.cuda.empty_cache()
+
+
+def fp8_report(torch, ops, args, steps=20, warmup=3):
+    """The batch-256 GQA decode step over FP8 E4M3 pools with a scale per
+    (block, kv head): the write encodes the step's bf16 K/V, the decode reads
+    1-byte codes.  KV GB/s counts the bytes the pools hold (1 per element)."""
+    from paged_kv_cache_330_amd.workloads import make_decode_workload
+    w = make_decode_workload(3)
+    st = fp8_step_state(torch, ops, w, args.pools, args.partition_tokens)
+    wall, t_copy, t_write, t_attn = time_steps(torch, st, steps, warmup)
+    B, Hq, Hkv, D, bs = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    res, _, _ = summary(w.name + "_fp8_e4m3", {"seed": w.seed, "kv_dtype": "fp8_e4m3",
+                                               "scales": "per (block, kv head), max-abs / 448"},
+                        w.seq_lens, B, Hq, Hkv, D, bs, steps, wall, t_copy, t_write, t_attn, es=1)
+    kv, alg = attn_bytes_fp8(w.seq_lens, B, Hq, Hkv, D, bs)
+    res["attn_alg_gbps"] = round(alg / (statistics.mean(t_attn) * 1e-3) / 1e9, 2)
+    res["attn_alg_hbm_frac"] = round(res["attn_alg_gbps"] / HBM_PEAK_GBPS, 4)
+    res["algorithmic_bytes_per_launch"] = alg
+    # the write reads bf16 K/V and the slots, writes 1-byte codes, reads scales
+    wb = B * Hkv * D * 2 * (2 + 1) + 8 * B + 2 * 4 * B * Hkv
+    res["write_gbps"] = round(wb / (statistics.median(t_write) * 1e-3) / 1e9, 2)
+    print(json.dumps({"report": res}), flush=True)
+    del st
+    torch.cuda.empty_cache()
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -600,6 +679,9 @@ def main():
     ops.load_library()
     if args.prefill:
         prefill_report(torch, ops)
+        return
+    if args.fp8:
+        fp8_report(torch, ops, args)
         return
     if args.report_all:
         report_all(torch, ops, args)

@@ -26,7 +26,9 @@
  *   - Base pointers of caches, K/V rows, q, out and workspace must be 16-byte
  *     aligned; int32/int64 arrays must be naturally aligned.
  *   - Supported: dtype PKV_F32 or PKV_BF16; head_dim 64 or 128; block_size
- *     8, 16, 32 or 64; num_q_heads / num_kv_heads in {1, 2, 4, 8}.
+ *     8, 16, 32 or 64; num_q_heads / num_kv_heads in {1, 2, 4, 8}.  Pools of
+ *     PKV_FP8_E4M3 codes have calls of their own (the *_fp8 calls below);
+ *     every other call rejects them with PKV_ERR_UNSUPPORTED.
  */
 #ifndef PAGEDKV_H_
 #define PAGEDKV_H_
@@ -38,7 +40,14 @@
 extern "C" {
 #endif
 
-typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+/*
+ * PKV_FP8_E4M3: one byte per element, the OCP 8-bit E4M3 format (1 sign bit,
+ * 4 exponent bits with bias 7, 3 mantissa bits; no infinities; S.1111.111 is
+ * NaN; largest finite magnitude 448), with one fp32 scale per (physical
+ * block, kv head) for K and one for V: a cached element is
+ * scale * value(code).
+ */
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 } pkv_dtype;
 
 typedef enum {
   PKV_OK = 0,
@@ -250,14 +259,78 @@ int pkv_attention_prefill(void* out, int32_t out_dtype, const void* q, int64_t n
                           int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
                           int32_t num_q_heads, float scale, void* stream);
 
+/*
+ * FP8 KV cache with a scale per block ("Paged KV" wiki, section "局限性": the
+ * page names an FP8 KV cache whose scaling factor is kept per block, and notes
+ * that such schemes tie the block size to the scale granularity; here the
+ * block is the scale group, so every supported block_size works).
+ *
+ * FP8 pools: k_cache, v_cache laid out as every pool, elements PKV_FP8_E4M3
+ * codes (cache->dtype must be PKV_FP8_E4M3; head_dim 64 or 128 for the
+ * write and the block moves, 128 for attention).  Scales: k_scale, v_scale
+ * [num_blocks][num_kv_heads] fp32, 4-byte aligned, owned by the caller, who
+ * sets a block's scales before its first token is written and keeps them
+ * while the block holds tokens (a scale is a property of the block, not of
+ * the token).
+ */
+
+/*
+ * Slot-mapping write into FP8 pools.  As pkv_kv_write, except that k and v are
+ * [num_tokens][num_kv_heads][head_dim] bf16 and element x of kv head h of a
+ * token whose slot lies in block blk is stored as the E4M3 code nearest to
+ * the binary32 quotient fl(x / scale[blk][h]) (ties to the even code,
+ * magnitudes beyond 448 saturate to 448, NaN stays NaN, -0 keeps its sign).
+ * A token row whose scale is not a positive finite number is not written and
+ * is flagged in the device error word.  Scales are only read.
+ */
+int pkv_kv_write_fp8(const void* k, const void* v, const int64_t* slot_mapping,
+                     int64_t num_tokens, void* k_cache, void* v_cache, const float* k_scale,
+                     const float* v_scale, const pkv_cache_desc* cache, void* stream);
+
+/*
+ * Decode attention over FP8 pools: the result pkv_attention_decode gives for
+ * pools holding the dequantized values scale * value(code) (fp32 arithmetic;
+ * q is bf16).  All other arguments, the workspace included, mean what they
+ * mean for pkv_attention_decode, whose pkv_attention_workspace_bytes sizes
+ * the workspace here too (with the FP8 descriptor).  Scales are used as
+ * given.
+ */
+int pkv_attention_decode_fp8(void* out, int32_t out_dtype, const void* q,
+                             const void* k_cache, const void* v_cache, const float* k_scale,
+                             const float* v_scale, const pkv_cache_desc* cache,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                             float scale, int32_t partition_tokens, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_block_copy for FP8 pools: each pair copies the K and V codes of the
+ * block and its num_kv_heads K and V scales, so that a copied block decodes
+ * to the same values.
+ */
+int pkv_block_copy_fp8(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                       const pkv_cache_desc* cache, const int64_t* src_dst_pairs,
+                       int64_t num_pairs, void* stream);
+
+/*
+ * pkv_block_transfer for FP8 pools: codes and scales of each pair move
+ * together.  The scale arrays follow the rules of their pools (device or
+ * pinned host memory, [num_blocks][num_kv_heads] fp32 of their own pool).
+ */
+int pkv_block_transfer_fp8(void* dst_k, void* dst_v, float* dst_k_scale, float* dst_v_scale,
+                           const pkv_cache_desc* dst_cache, const void* src_k, const void* src_v,
+                           const float* src_k_scale, const float* src_v_scale,
+                           const pkv_cache_desc* src_cache, const int64_t* src_dst_pairs,
+                           int64_t num_pairs, void* stream);
+
 /* Message for the last non-OK return on this thread ("" if none). */
 const char* pkv_last_error(void);
 
 /*
  * Synchronises `stream`, then reads and clears the current device's error
  * word.  Returns PKV_OK if no kernel recorded a bad slot, block id, sequence
- * length, copy pair, shared-prefix description or prefill query range since the
- * last check;
+ * length, copy pair, shared-prefix description, prefill query range or FP8
+ * scale since the last check;
  * otherwise PKV_ERR_INVALID_ARG with the offending kinds in pkv_last_error().
  */
 int pkv_check_device_errors(void* stream);

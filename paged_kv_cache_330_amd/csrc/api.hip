@@ -67,20 +67,34 @@ int error_word(unsigned** out) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-int elem_bytes(int32_t dtype) { return dtype == PKV_F32 ? 4 : 2; }
+int elem_bytes(int32_t dtype) { return dtype == PKV_F32 ? 4 : dtype == PKV_BF16 ? 2 : 1; }
 
 int check_cache(const pkv_cache_desc* c) {
   if (!c) return fail(PKV_ERR_INVALID_ARG, "cache descriptor is NULL");
   if (c->num_blocks < 0 || c->num_blocks > (int64_t(1) << 40))
     return fail(PKV_ERR_INVALID_ARG, "num_blocks %lld out of range", (long long)c->num_blocks);
-  if (c->dtype != PKV_F32 && c->dtype != PKV_BF16)
-    return fail(PKV_ERR_UNSUPPORTED, "cache dtype %d is neither PKV_F32 nor PKV_BF16", c->dtype);
+  if (c->dtype != PKV_F32 && c->dtype != PKV_BF16 && c->dtype != PKV_FP8_E4M3)
+    return fail(PKV_ERR_UNSUPPORTED, "cache dtype %d is not PKV_F32, PKV_BF16 or PKV_FP8_E4M3",
+                c->dtype);
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(PKV_ERR_UNSUPPORTED, "head_dim %d is not 64 or 128", c->head_dim);
   if (c->block_size != 8 && c->block_size != 16 && c->block_size != 32 && c->block_size != 64)
     return fail(PKV_ERR_UNSUPPORTED, "block_size %d is not 8, 16, 32 or 64", c->block_size);
   if (c->num_kv_heads < 1 || c->num_kv_heads > 1024)
     return fail(PKV_ERR_INVALID_ARG, "num_kv_heads %d out of range", c->num_kv_heads);
+  return PKV_OK;
+}
+
+// FP8 pools go through the *_fp8 calls, which also take their scales.
+int check_not_fp8(const pkv_cache_desc* c, const char* call) {
+  if (c->dtype == PKV_FP8_E4M3)
+    return fail(PKV_ERR_UNSUPPORTED, "%s does not take PKV_FP8_E4M3 pools; use %s_fp8", call, call);
+  return PKV_OK;
+}
+
+int check_fp8(const pkv_cache_desc* c, const char* call) {
+  if (c->dtype != PKV_FP8_E4M3)
+    return fail(PKV_ERR_UNSUPPORTED, "%s takes PKV_FP8_E4M3 pools only", call);
   return PKV_OK;
 }
 
@@ -158,9 +172,11 @@ int make_plan(const pkv_cache_desc* cache, int32_t num_seqs, int32_t num_q_heads
   if (p->max_parts > 65535)
     return fail(PKV_ERR_INVALID_ARG, "%lld partitions per sequence exceed 65535",
                 (long long)p->max_parts);
-  // The balanced schedule serves the automatic choice for the bf16 head_dim
-  // 128 kernels; an explicit partition size asks for the partition grid.
-  const bool balanced = partition_tokens == 0 && cache->dtype == PKV_BF16 &&
+  // The balanced schedule serves the automatic choice for the head_dim 128
+  // matrix-core kernels (bf16 and FP8 pools); an explicit partition size asks
+  // for the partition grid.
+  const bool balanced = partition_tokens == 0 &&
+                        (cache->dtype == PKV_BF16 || cache->dtype == PKV_FP8_E4M3) &&
                         cache->head_dim == 128 && num_seqs <= pkv::kMaxBalancedSeqs &&
                         num_seqs > 0;
   p->slices = balanced ? pkv::balanced_slices(cache->num_kv_heads) : 0;
@@ -280,6 +296,7 @@ int pkv_kv_write(const void* k, const void* v, const int64_t* slot_mapping, int6
                  void* k_cache, void* v_cache, const pkv_cache_desc* cache, void* stream) {
   g_last_error.clear();
   PKV_TRY(check_cache(cache));
+  PKV_TRY(check_not_fp8(cache, "pkv_kv_write"));
   if (num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "num_tokens %lld < 0", (long long)num_tokens);
   if (num_tokens == 0) return PKV_OK;
   PKV_TRY(check_ptr(k, 16, "k"));
@@ -301,6 +318,7 @@ int pkv_block_copy(void* k_cache, void* v_cache, const pkv_cache_desc* cache,
                    const int64_t* src_dst_pairs, int64_t num_pairs, void* stream) {
   g_last_error.clear();
   PKV_TRY(check_cache(cache));
+  PKV_TRY(check_not_fp8(cache, "pkv_block_copy"));
   if (num_pairs < 0) return fail(PKV_ERR_INVALID_ARG, "num_pairs %lld < 0", (long long)num_pairs);
   if (num_pairs == 0) return PKV_OK;
   PKV_TRY(check_ptr(src_dst_pairs, 8, "src_dst_pairs"));
@@ -322,6 +340,7 @@ int pkv_block_transfer(void* dst_k, void* dst_v, const pkv_cache_desc* dst_cache
   g_last_error.clear();
   PKV_TRY(check_cache(dst_cache));
   PKV_TRY(check_cache(src_cache));
+  PKV_TRY(check_not_fp8(src_cache, "pkv_block_transfer"));
   if (dst_cache->block_size != src_cache->block_size ||
       dst_cache->num_kv_heads != src_cache->num_kv_heads ||
       dst_cache->head_dim != src_cache->head_dim || dst_cache->dtype != src_cache->dtype)
@@ -375,6 +394,7 @@ int pkv_attention_decode(void* out, int32_t out_dtype, const void* q, const void
   g_last_error.clear();
   Plan plan;
   PKV_TRY(make_plan(cache, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, &plan));
+  PKV_TRY(check_not_fp8(cache, "pkv_attention_decode"));
   PKV_TRY(check_decode_scalars(cache, num_q_heads, out_dtype, scale));
   if (num_seqs == 0) return PKV_OK;
   pkv::DecodeArgs a{};
@@ -463,6 +483,151 @@ int pkv_attention_prefill(void* out, int32_t out_dtype, const void* q, int64_t n
   return e == hipSuccess ? PKV_OK : hip_fail(e, "attention_prefill launch");
 }
 
+int pkv_kv_write_fp8(const void* k, const void* v, const int64_t* slot_mapping,
+                     int64_t num_tokens, void* k_cache, void* v_cache, const float* k_scale,
+                     const float* v_scale, const pkv_cache_desc* cache, void* stream) {
+  g_last_error.clear();
+  PKV_TRY(check_cache(cache));
+  PKV_TRY(check_fp8(cache, "pkv_kv_write_fp8"));
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "num_tokens %lld < 0", (long long)num_tokens);
+  if (num_tokens == 0) return PKV_OK;
+  PKV_TRY(check_ptr(k, 16, "k"));
+  PKV_TRY(check_ptr(v, 16, "v"));
+  PKV_TRY(check_ptr(slot_mapping, 8, "slot_mapping"));
+  PKV_TRY(check_ptr(k_cache, 16, "k_cache"));
+  PKV_TRY(check_ptr(v_cache, 16, "v_cache"));
+  PKV_TRY(check_ptr(k_scale, 4, "k_scale"));
+  PKV_TRY(check_ptr(v_scale, 4, "v_scale"));
+  unsigned* err = nullptr;
+  PKV_TRY(error_word(&err));
+  hipError_t e = pkv::launch_kv_write_fp8(k, v, slot_mapping, num_tokens, k_cache, v_cache,
+                                          k_scale, v_scale, cache->num_blocks * cache->block_size,
+                                          cache->block_size, cache->num_kv_heads, cache->head_dim,
+                                          err, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "kv_write_fp8 launch");
+}
+
+int pkv_attention_decode_fp8(void* out, int32_t out_dtype, const void* q, const void* k_cache,
+                             const void* v_cache, const float* k_scale, const float* v_scale,
+                             const pkv_cache_desc* cache, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                             int32_t num_seqs, int32_t num_q_heads, float scale,
+                             int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  g_last_error.clear();
+  Plan plan;
+  PKV_TRY(make_plan(cache, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, &plan));
+  PKV_TRY(check_fp8(cache, "pkv_attention_decode_fp8"));
+  if (cache->head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "FP8 decode needs head_dim 128, got %d", cache->head_dim);
+  PKV_TRY(check_decode_scalars(cache, num_q_heads, out_dtype, scale));
+  if (num_seqs == 0) return PKV_OK;
+  pkv::DecodeArgs a{};
+  PKV_TRY(fill_decode_args(out, out_dtype, q, k_cache, v_cache, cache, block_tables,
+                           max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, scale, &a));
+  PKV_TRY(check_ptr(k_scale, 4, "k_scale"));
+  PKV_TRY(check_ptr(v_scale, 4, "v_scale"));
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  PKV_TRY(attach_workspace(workspace, workspace_bytes, plan.workspace, plan.layout, &a));
+  PKV_TRY(error_word(&a.err));
+  a.part_tokens = plan.part;
+  a.max_parts = static_cast<int32_t>(plan.max_parts);
+  a.slices = plan.slices;
+  hipError_t e = pkv::launch_decode(a, 0, cache->head_dim, cache->block_size,
+                                    num_q_heads / cache->num_kv_heads,
+                                    static_cast<hipStream_t>(stream), true);
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "attention_decode_fp8 launch");
+}
+
+int pkv_block_copy_fp8(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                       const pkv_cache_desc* cache, const int64_t* src_dst_pairs,
+                       int64_t num_pairs, void* stream) {
+  g_last_error.clear();
+  PKV_TRY(check_cache(cache));
+  PKV_TRY(check_fp8(cache, "pkv_block_copy_fp8"));
+  if (num_pairs < 0) return fail(PKV_ERR_INVALID_ARG, "num_pairs %lld < 0", (long long)num_pairs);
+  if (num_pairs == 0) return PKV_OK;
+  PKV_TRY(check_ptr(src_dst_pairs, 8, "src_dst_pairs"));
+  PKV_TRY(check_ptr(k_cache, 16, "k_cache"));
+  PKV_TRY(check_ptr(v_cache, 16, "v_cache"));
+  PKV_TRY(check_ptr(k_scale, 4, "k_scale"));
+  PKV_TRY(check_ptr(v_scale, 4, "v_scale"));
+  unsigned* err = nullptr;
+  PKV_TRY(error_word(&err));
+  const int64_t block_bytes = static_cast<int64_t>(cache->block_size) * cache->num_kv_heads *
+                              cache->head_dim * elem_bytes(cache->dtype);
+  pkv::BlockScales sc;
+  sc.dst_ks = k_scale;
+  sc.dst_vs = v_scale;
+  sc.src_ks = k_scale;
+  sc.src_vs = v_scale;
+  sc.scales = cache->num_kv_heads;
+  hipError_t e = pkv::launch_block_copy(k_cache, v_cache, k_cache, v_cache, src_dst_pairs,
+                                        num_pairs, cache->num_blocks, cache->num_blocks,
+                                        block_bytes, err, static_cast<hipStream_t>(stream), sc);
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "block_copy_fp8 launch");
+}
+
+int pkv_block_transfer_fp8(void* dst_k, void* dst_v, float* dst_k_scale, float* dst_v_scale,
+                           const pkv_cache_desc* dst_cache, const void* src_k, const void* src_v,
+                           const float* src_k_scale, const float* src_v_scale,
+                           const pkv_cache_desc* src_cache, const int64_t* src_dst_pairs,
+                           int64_t num_pairs, void* stream) {
+  g_last_error.clear();
+  PKV_TRY(check_cache(dst_cache));
+  PKV_TRY(check_cache(src_cache));
+  PKV_TRY(check_fp8(src_cache, "pkv_block_transfer_fp8"));
+  if (dst_cache->block_size != src_cache->block_size ||
+      dst_cache->num_kv_heads != src_cache->num_kv_heads ||
+      dst_cache->head_dim != src_cache->head_dim || dst_cache->dtype != src_cache->dtype)
+    return fail(PKV_ERR_INVALID_ARG, "source and destination pools differ in block shape or dtype");
+  if (num_pairs < 0) return fail(PKV_ERR_INVALID_ARG, "num_pairs %lld < 0", (long long)num_pairs);
+  if (num_pairs == 0) return PKV_OK;
+  PKV_TRY(check_ptr(src_dst_pairs, 8, "src_dst_pairs"));
+  PKV_TRY(check_ptr(dst_k, 16, "dst_k"));
+  PKV_TRY(check_ptr(dst_v, 16, "dst_v"));
+  PKV_TRY(check_ptr(src_k, 16, "src_k"));
+  PKV_TRY(check_ptr(src_v, 16, "src_v"));
+  PKV_TRY(check_ptr(dst_k_scale, 4, "dst_k_scale"));
+  PKV_TRY(check_ptr(dst_v_scale, 4, "dst_v_scale"));
+  PKV_TRY(check_ptr(src_k_scale, 4, "src_k_scale"));
+  PKV_TRY(check_ptr(src_v_scale, 4, "src_v_scale"));
+  void* dk = nullptr;
+  void* dv = nullptr;
+  const void* sk = nullptr;
+  const void* sv = nullptr;
+  void* dks = nullptr;
+  void* dvs = nullptr;
+  const void* sks = nullptr;
+  const void* svs = nullptr;
+  PKV_TRY(device_address(dst_k, "dst_k", &dk));
+  PKV_TRY(device_address(dst_v, "dst_v", &dv));
+  PKV_TRY(device_address(src_k, "src_k", const_cast<void**>(&sk)));
+  PKV_TRY(device_address(src_v, "src_v", const_cast<void**>(&sv)));
+  PKV_TRY(device_address(dst_k_scale, "dst_k_scale", &dks));
+  PKV_TRY(device_address(dst_v_scale, "dst_v_scale", &dvs));
+  PKV_TRY(device_address(src_k_scale, "src_k_scale", const_cast<void**>(&sks)));
+  PKV_TRY(device_address(src_v_scale, "src_v_scale", const_cast<void**>(&svs)));
+  void* pairs_dev = nullptr;
+  PKV_TRY(device_address(src_dst_pairs, "src_dst_pairs", &pairs_dev));
+  unsigned* err = nullptr;
+  PKV_TRY(error_word(&err));
+  const int64_t block_bytes = static_cast<int64_t>(src_cache->block_size) *
+                              src_cache->num_kv_heads * src_cache->head_dim *
+                              elem_bytes(src_cache->dtype);
+  pkv::BlockScales sc;
+  sc.dst_ks = static_cast<float*>(dks);
+  sc.dst_vs = static_cast<float*>(dvs);
+  sc.src_ks = static_cast<const float*>(sks);
+  sc.src_vs = static_cast<const float*>(svs);
+  sc.scales = src_cache->num_kv_heads;
+  hipError_t e = pkv::launch_block_copy(dk, dv, sk, sv, static_cast<const int64_t*>(pairs_dev),
+                                        num_pairs, src_cache->num_blocks, dst_cache->num_blocks,
+                                        block_bytes, err, static_cast<hipStream_t>(stream), sc);
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "block_transfer_fp8 launch");
+}
+
 int pkv_check_device_errors(void* stream) {
   g_last_error.clear();
   unsigned* err = nullptr;
@@ -476,13 +641,14 @@ int pkv_check_device_errors(void* stream) {
   const unsigned zero = 0;
   e = hipMemcpy(err, &zero, sizeof(zero), hipMemcpyHostToDevice);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpy(clear error word)");
-  return fail(PKV_ERR_INVALID_ARG, "device range checks failed:%s%s%s%s%s%s",
+  return fail(PKV_ERR_INVALID_ARG, "device range checks failed:%s%s%s%s%s%s%s",
               (word & pkv::kErrSlot) ? " slot>=num_blocks*block_size" : "",
               (word & pkv::kErrBlockId) ? " block_id_out_of_range" : "",
               (word & pkv::kErrSeqLen) ? " seq_len_out_of_range" : "",
               (word & pkv::kErrCopyPair) ? " copy_pair_out_of_range" : "",
               (word & pkv::kErrShared) ? " shared_prefix_inconsistent" : "",
-              (word & pkv::kErrQuery) ? " prefill_query_range_inconsistent" : "");
+              (word & pkv::kErrQuery) ? " prefill_query_range_inconsistent" : "",
+              (word & pkv::kErrScale) ? " fp8_scale_not_positive_finite" : "");
 }
 
 }  // extern "C"

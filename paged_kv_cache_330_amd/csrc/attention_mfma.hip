@@ -20,7 +20,7 @@ namespace {
 // dispatched from the last to the first so that the full partitions of long
 // sequences start early and the short tails of short ones fill the end.
 // ----------------------------------------------------------------------------
-template <int G, int BS, int TC>
+template <int G, int BS, int TC, bool F8>
 __global__ __launch_bounds__(kMaxWaves * 64) void decode_mfma_kernel(DecodeArgs a) {
   static_assert(16 % G == 0, "group must divide 16");
   __shared__ int s_bt[kMaxPartitionTokens / BS + 1];
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mfma_kernel(DecodeArgs 
   load_query<G>(a, b, kvh, lane & 15, lane >> 4, qop);
   WaveState<G> st;
   st.reset();
-  attend_range<G, BS, TC>(a, s_bt, s_kt + (PKV_K_VIA_LDS ? wave * 16 * kKRowPad : 0),
+  attend_range<G, BS, TC, F8>(a, s_bt, s_kt + (PKV_K_VIA_LDS ? wave * 16 * kKRowPad : 0),
                           s_vt + (kPvOnMfma<G> ? wave * 16 * kKRowPad : 0), b, kvh, pt.begin,
                           pt.end, qop, st);
   Sink sink{nullptr, nullptr, nullptr, 0, 0};
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mfma_kernel(DecodeArgs 
 // sequence (its first piece); its merge descriptor ws_desc[slice] names that
 // sequence and the slice of its first piece, or -1.
 // ----------------------------------------------------------------------------
-template <int G, int BS, int TC>
+template <int G, int BS, int TC, bool F8>
 __global__ __launch_bounds__(kMaxWaves * 64) PKV_BALANCED_OCCUPANCY void decode_balanced_kernel(
     DecodeArgs a) {
   static_assert(16 % G == 0, "group must divide 16");
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) PKV_BALANCED_OCCUPANCY void decode_
     load_query<G>(a, b, kvh, lane & 15, lane >> 4, qop);
     WaveState<G> st;
     st.reset();
-    attend_range<G, BS, TC>(a, s_bt, s_kt + (PKV_K_VIA_LDS ? wave * 16 * kKRowPad : 0),
+    attend_range<G, BS, TC, F8>(a, s_bt, s_kt + (PKV_K_VIA_LDS ? wave * 16 * kKRowPad : 0),
                             s_vt + (kPvOnMfma<G> ? wave * 16 * kKRowPad : 0), b, kvh, tok_begin,
                             tok_end, qop, st);
     Sink sink{nullptr, nullptr, nullptr, 0, 0};
@@ -212,31 +212,31 @@ __global__ __launch_bounds__(kMaxWaves * 64) void balanced_reduce_kernel(DecodeA
   }
 }
 
-template <int G>
+template <int G, bool F8>
 hipError_t launch_partitions_g(const DecodeArgs& a, int block_size, int kh, hipStream_t s) {
   constexpr int TC = PKV_MFMA_TILE_CHUNKS;
   const dim3 grid(a.num_kv_heads / kh, a.num_seqs, a.max_parts);
   const dim3 block(kh * 64);
   switch (block_size) {
-    case 8: decode_mfma_kernel<G, 8, TC><<<grid, block, 0, s>>>(a); break;
-    case 16: decode_mfma_kernel<G, 16, TC><<<grid, block, 0, s>>>(a); break;
-    case 32: decode_mfma_kernel<G, 32, TC><<<grid, block, 0, s>>>(a); break;
-    case 64: decode_mfma_kernel<G, 64, TC><<<grid, block, 0, s>>>(a); break;
+    case 8: decode_mfma_kernel<G, 8, TC, F8><<<grid, block, 0, s>>>(a); break;
+    case 16: decode_mfma_kernel<G, 16, TC, F8><<<grid, block, 0, s>>>(a); break;
+    case 32: decode_mfma_kernel<G, 32, TC, F8><<<grid, block, 0, s>>>(a); break;
+    case 64: decode_mfma_kernel<G, 64, TC, F8><<<grid, block, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <int G>
+template <int G, bool F8>
 hipError_t launch_balanced_g(const DecodeArgs& a, int block_size, int kh, hipStream_t s) {
   constexpr int TC = PKV_MFMA_TILE_CHUNKS;
   const dim3 grid(a.num_kv_heads / kh, a.slices);
   const dim3 block(kh * 64);
   switch (block_size) {
-    case 8: decode_balanced_kernel<G, 8, TC><<<grid, block, 0, s>>>(a); break;
-    case 16: decode_balanced_kernel<G, 16, TC><<<grid, block, 0, s>>>(a); break;
-    case 32: decode_balanced_kernel<G, 32, TC><<<grid, block, 0, s>>>(a); break;
-    case 64: decode_balanced_kernel<G, 64, TC><<<grid, block, 0, s>>>(a); break;
+    case 8: decode_balanced_kernel<G, 8, TC, F8><<<grid, block, 0, s>>>(a); break;
+    case 16: decode_balanced_kernel<G, 16, TC, F8><<<grid, block, 0, s>>>(a); break;
+    case 32: decode_balanced_kernel<G, 32, TC, F8><<<grid, block, 0, s>>>(a); break;
+    case 64: decode_balanced_kernel<G, 64, TC, F8><<<grid, block, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
@@ -253,25 +253,36 @@ int mfma_waves_per_group(int num_kv_heads) {
   return 1;
 }
 
-hipError_t launch_mfma_decode(const DecodeArgs& a, int block_size, int group, hipStream_t s) {
+namespace {
+
+template <bool F8>
+hipError_t launch_mfma_typed(const DecodeArgs& a, int block_size, int group, hipStream_t s) {
   const int kh = mfma_waves_per_group(a.num_kv_heads);
   if (a.slices > 0) {
     if (a.num_seqs > kMaxBalancedSeqs) return hipErrorInvalidValue;
     switch (group) {
-      case 1: return launch_balanced_g<1>(a, block_size, kh, s);
-      case 2: return launch_balanced_g<2>(a, block_size, kh, s);
-      case 4: return launch_balanced_g<4>(a, block_size, kh, s);
-      case 8: return launch_balanced_g<8>(a, block_size, kh, s);
+      case 1: return launch_balanced_g<1, F8>(a, block_size, kh, s);
+      case 2: return launch_balanced_g<2, F8>(a, block_size, kh, s);
+      case 4: return launch_balanced_g<4, F8>(a, block_size, kh, s);
+      case 8: return launch_balanced_g<8, F8>(a, block_size, kh, s);
       default: return hipErrorInvalidValue;
     }
   }
   switch (group) {
-    case 1: return launch_partitions_g<1>(a, block_size, kh, s);
-    case 2: return launch_partitions_g<2>(a, block_size, kh, s);
-    case 4: return launch_partitions_g<4>(a, block_size, kh, s);
-    case 8: return launch_partitions_g<8>(a, block_size, kh, s);
+    case 1: return launch_partitions_g<1, F8>(a, block_size, kh, s);
+    case 2: return launch_partitions_g<2, F8>(a, block_size, kh, s);
+    case 4: return launch_partitions_g<4, F8>(a, block_size, kh, s);
+    case 8: return launch_partitions_g<8, F8>(a, block_size, kh, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+}  // namespace
+
+hipError_t launch_mfma_decode(const DecodeArgs& a, int block_size, int group, hipStream_t s,
+                              bool fp8) {
+  return fp8 ? launch_mfma_typed<true>(a, block_size, group, s)
+             : launch_mfma_typed<false>(a, block_size, group, s);
 }
 
 }  // namespace pkv

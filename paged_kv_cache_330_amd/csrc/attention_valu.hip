@@ -202,10 +202,11 @@ hipError_t launch_valu(const DecodeArgs& a, int block_size, int group, hipStream
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, int bf16, int head_dim, int block_size, int group,
-                         hipStream_t stream) {
+                         hipStream_t stream, bool fp8) {
   hipError_t e = hipErrorInvalidValue;
-  if (bf16 && head_dim == 128) {
-    e = launch_mfma_decode(a, block_size, group, stream);
+  if (fp8 && head_dim != 128) return hipErrorInvalidValue;
+  if ((bf16 || fp8) && head_dim == 128) {
+    e = launch_mfma_decode(a, block_size, group, stream, fp8);
     if (e != hipSuccess || a.slices > 0) return e;  // the balanced schedule has its own reduce
   } else if (a.slices > 0) {
     return hipErrorInvalidValue;

@@ -7,8 +7,9 @@
 // when device memory runs short, inactive blocks move to CPU memory and are
 // loaded back when needed.  The host block manager decides the (src, dst)
 // pairs; this kernel copies the K block and the V block of each pair, all
-// block_size slots, as 16-byte vectors.  Grid: x = pair, y = slice of the
-// block, z = 0 for K / 1 for V.
+// block_size slots, as 16-byte vectors, and for FP8 pools the block's per-head
+// scales with it.  Grid: x = pair, y = slice of the block, z = 0 for K / 1
+// for V.
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -17,7 +18,7 @@ namespace {
 __global__ __launch_bounds__(256) void block_copy_kernel(
     uint4* dst_k, uint4* dst_v, const uint4* src_k, const uint4* src_v,
     const int64_t* __restrict__ pairs, int64_t src_blocks, int64_t dst_blocks,
-    int64_t block_vecs, unsigned* err) {
+    int64_t block_vecs, unsigned* err, BlockScales sc) {
   const int64_t p = blockIdx.x;
   const int64_t src = pairs[2 * p];
   const int64_t dst = pairs[2 * p + 1];
@@ -28,6 +29,11 @@ __global__ __launch_bounds__(256) void block_copy_kernel(
   }
   const uint4* s = (blockIdx.z ? src_v : src_k) + src * block_vecs;
   uint4* d = (blockIdx.z ? dst_v : dst_k) + dst * block_vecs;
+  if (sc.src_ks && blockIdx.y == 0) {
+    const float* ss = (blockIdx.z ? sc.src_vs : sc.src_ks) + src * sc.scales;
+    float* ds = (blockIdx.z ? sc.dst_vs : sc.dst_ks) + dst * sc.scales;
+    for (int i = threadIdx.x; i < sc.scales; i += blockDim.x) ds[i] = ss[i];
+  }
   const int64_t stride = static_cast<int64_t>(gridDim.y) * blockDim.x;
   for (int64_t i = static_cast<int64_t>(blockIdx.y) * blockDim.x + threadIdx.x; i < block_vecs;
        i += stride)
@@ -39,7 +45,7 @@ __global__ __launch_bounds__(256) void block_copy_kernel(
 hipError_t launch_block_copy(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
                              const int64_t* pairs, int64_t num_pairs, int64_t src_blocks,
                              int64_t dst_blocks, int64_t block_bytes, unsigned* err,
-                             hipStream_t stream) {
+                             hipStream_t stream, const BlockScales& sc) {
   const int threads = 256;
   const int64_t block_vecs = block_bytes / 16;
   int64_t slices = (block_vecs + threads - 1) / threads;
@@ -48,7 +54,7 @@ hipError_t launch_block_copy(void* dst_k, void* dst_v, const void* src_k, const 
   block_copy_kernel<<<dim3(static_cast<unsigned>(num_pairs), static_cast<unsigned>(slices), 2),
                       dim3(threads), 0, stream>>>(
       static_cast<uint4*>(dst_k), static_cast<uint4*>(dst_v), static_cast<const uint4*>(src_k),
-      static_cast<const uint4*>(src_v), pairs, src_blocks, dst_blocks, block_vecs, err);
+      static_cast<const uint4*>(src_v), pairs, src_blocks, dst_blocks, block_vecs, err, sc);
   return hipGetLastError();
 }
 

@@ -63,11 +63,57 @@ constexpr int kMaxWaves = 8;
 #define PKV_BALANCED_OCCUPANCY
 #endif
 
-// K and V rows of one tile (TC chunks of 16 tokens) of one wave.
+// Eight E4M3 codes widened to eight bf16 values, exactly (an E4M3 value has
+// at most 4 significant bits); gfx950's conversion decodes OCP E4M3.
+__device__ __forceinline__ u32x4_t widen_e4m3(u32x2_t w) {
+  u32x4_t r;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], false);  // codes 4j, 4j + 1
+    const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], true);   // codes 4j + 2, 4j + 3
+    r[2 * j] = __builtin_amdgcn_perm(__float_as_uint(lo.y), __float_as_uint(lo.x), 0x07060302u);
+    r[2 * j + 1] = __builtin_amdgcn_perm(__float_as_uint(hi.y), __float_as_uint(hi.x), 0x07060302u);
+  }
+  return r;
+}
+
+// K and V rows of one tile (TC chunks of 16 tokens) of one wave: for bf16
+// pools 16 bytes (8 elements) of each of 4 rows per lane; for FP8 pools 8
+// bytes (the same 8 elements) of each row and the K and V scales of the
+// rows' block.  krow/vrow give the rows as bf16.
+template <int TC, bool F8 = false>
+struct KVTile;
+
 template <int TC>
-struct KVTile {
+struct KVTile<TC, false> {
   u32x4_t k[TC][4];
   u32x4_t v[TC][4];
+  __device__ __forceinline__ u32x4_t krow(int c, int i) const { return k[c][i]; }
+  __device__ __forceinline__ u32x4_t vrow(int c, int i) const { return v[c][i]; }
+  // An empty asm on every loaded register (see stream_window).
+  __device__ __forceinline__ void pin() {
+#pragma unroll
+    for (int ch = 0; ch < TC; ++ch)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(k[ch][s]), "+v"(v[ch][s]));
+  }
+};
+
+template <int TC>
+struct KVTile<TC, true> {
+  u32x2_t k[TC][4];
+  u32x2_t v[TC][4];
+  float ks[TC], vs[TC];  // scales of the block of this lane's rows
+  __device__ __forceinline__ u32x4_t krow(int c, int i) const { return widen_e4m3(k[c][i]); }
+  __device__ __forceinline__ u32x4_t vrow(int c, int i) const { return widen_e4m3(v[c][i]); }
+  __device__ __forceinline__ void pin() {
+#pragma unroll
+    for (int ch = 0; ch < TC; ++ch) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(k[ch][s]), "+v"(v[ch][s]));
+      asm volatile("" : "+v"(ks[ch]), "+v"(vs[ch]));
+    }
+  }
 };
 
 // With PKV_K_VIA_LDS the K rows are loaded like the V rows (each load
@@ -82,6 +128,11 @@ struct TileCtx {
   const uint16_t* vbase;  // V pool + kv head offset + this lane's dims
   const uint16_t* kdead;  // this wave's query row + this lane's offset (see load_tile)
   const uint16_t* vdead;  // this wave's query row + this lane's dims
+  const uint8_t* kbase8;  // FP8 pools: K pool + kv head offset + this lane's dims
+  const uint8_t* vbase8;  // FP8 pools: V pool + kv head offset + this lane's dims
+  const float* kscale;    // FP8 pools: scales [num_blocks][num_kv_heads] + kv head
+  const float* vscale;
+  int scale_stride;       // FP8 pools: num_kv_heads
   u32x4_t* k_lds;         // this wave's K transpose tile (PKV_K_VIA_LDS)
   u32x4_t* v_lds;         // this wave's V tile, read column-wise (P.V on the matrix cores)
   int64_t tok_stride;     // elements between consecutive slots
@@ -102,14 +153,24 @@ __device__ __forceinline__ u32x4_t load_kv(const uint16_t* p) {
 #endif
 }
 
+// 8 bytes of an FP8 row, with the streaming hint like load_kv.
+__device__ __forceinline__ u32x2_t load_kv8(const uint8_t* p) {
+#if PKV_KV_NONTEMPORAL
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+#else
+  return *reinterpret_cast<const u32x2_t*>(p);
+#endif
+}
+
 // Issue the loads of the tile starting at token t0.  Tokens past the end of
 // the window re-read its last token, so every address is a valid row (the
 // scores of such tokens are masked to -inf).  A chunk wholly past the end
 // (the prefetch after a window's last tile, never computed) reads this
 // wave's 256-byte query row instead, which is in cache, so it costs no HBM
-// traffic.
-template <int BS, int TC>
-__device__ __forceinline__ void load_tile(KVTile<TC>& r, int t0, const TileCtx& c) {
+// traffic.  FP8 pools: a lane's 4 rows (4 qr .. 4 qr + 3, clamped to the
+// window's last token) always lie in one block, whose scales it loads too.
+template <int BS, int TC, bool F8 = false>
+__device__ __forceinline__ void load_tile(KVTile<TC, F8>& r, int t0, const TileCtx& c) {
 #pragma unroll
   for (int ch = 0; ch < TC; ++ch) {
     const bool dead = t0 + 16 * ch > c.last_chunk;
@@ -132,10 +193,21 @@ __device__ __forceinline__ void load_tile(KVTile<TC>& r, int t0, const TileCtx& 
     for (int i = 0; i < 4; ++i) {  // row 4 qr + i, dims 8 col .. 8 col + 7
       const int tv = min(tce + 4 * c.qr + i, c.end - 1);
       const int64_t row = ((int64_t)pv[i] * BS + (tv & (BS - 1))) * c.tok_stride;
-      r.k[ch][i] = load_kv(dead ? c.kdead : c.kbase + row);
-      r.v[ch][i] = load_kv(dead ? c.vdead : c.vbase + row);
+      if constexpr (F8) {
+        r.k[ch][i] = load_kv8(dead ? reinterpret_cast<const uint8_t*>(c.kdead) : c.kbase8 + row);
+        r.v[ch][i] = load_kv8(dead ? reinterpret_cast<const uint8_t*>(c.vdead) : c.vbase8 + row);
+      } else {
+        r.k[ch][i] = load_kv(dead ? c.kdead : c.kbase + row);
+        r.v[ch][i] = load_kv(dead ? c.vdead : c.vbase + row);
+      }
+    }
+    if constexpr (F8) {
+      const int64_t si = (int64_t)(dead ? 0 : pv[0]) * c.scale_stride;
+      r.ks[ch] = c.kscale[si];
+      r.vs[ch] = c.vscale[si];
     }
 #else
+    static_assert(!F8, "FP8 pools load K rows like V rows");
     const uint16_t* kp =
         dead ? c.kdead : c.kbase + ((int64_t)pk * BS + (tk & (BS - 1))) * c.tok_stride;
 #pragma unroll
@@ -212,8 +284,8 @@ struct CausalTokens {
 // scale * log2(e); tokens the columns do not attend to (at or past `end`, or
 // past a column's limit) score -inf.  mt[n] is the tile's maximum of set n
 // over each column (all four row groups).
-template <int TC, int NS, class Lim = WindowTokens>
-__device__ __forceinline__ void tile_scores(const KVTile<TC>& r, int t0, int end,
+template <int TC, int NS, bool F8, class Lim = WindowTokens>
+__device__ __forceinline__ void tile_scores(const KVTile<TC, F8>& r, int t0, int end,
                                             const bf16x8_t (&qop)[NS][4], float scale_log2e,
                                             const TileCtx& ctx, float (&x)[NS][TC][4],
                                             float (&mt)[NS], const Lim& lim = Lim{}) {
@@ -226,12 +298,12 @@ __device__ __forceinline__ void tile_scores(const KVTile<TC>& r, int t0, int end
 #if PKV_K_VIA_LDS
     // rows as loaded -> LDS -> lane (col, qr) takes d-chunk 4 s + qr of row col
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ctx.k_lds[(4 * qr + i) * kKRowPad + ctx.col] = r.k[c][i];
+    for (int i = 0; i < 4; ++i) ctx.k_lds[(4 * qr + i) * kKRowPad + ctx.col] = r.krow(c, i);
 #pragma unroll
     for (int s = 0; s < 4; ++s) kop[s] = ctx.k_lds[ctx.col * kKRowPad + 4 * s + qr];
 #else
 #pragma unroll
-    for (int s = 0; s < 4; ++s) kop[s] = r.k[c][s];
+    for (int s = 0; s < 4; ++s) kop[s] = r.krow(c, s);
 #endif
 #pragma unroll
     for (int n = 0; n < NS; ++n) {
@@ -240,10 +312,12 @@ __device__ __forceinline__ void tile_scores(const KVTile<TC>& r, int t0, int end
       for (int s = 0; s < 4; ++s)
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop[s]),
                                                         qop[n][s], sacc, 0, 0, 0);
+      float sl = scale_log2e;
+      if constexpr (F8) sl *= r.ks[c];  // dequantised K = scale * code value
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = t0 + 16 * c + 4 * qr + i;
-        x[n][c][i] = lim.valid(n, tok, end) ? sacc[i] * scale_log2e : -INFINITY;
+        x[n][c][i] = lim.valid(n, tok, end) ? sacc[i] * sl : -INFINITY;
         mt[n] = fmaxf(mt[n], x[n][c][i]);
       }
     }
@@ -277,8 +351,8 @@ __device__ __forceinline__ float softmax_update(float (&x)[TC][4], float mt, flo
 
 // Scores, online-softmax update and P.V accumulation for one loaded tile,
 // P.V on the matrix cores.
-template <int TC, int NS, class Lim = WindowTokens>
-__device__ __forceinline__ void compute_tile(const KVTile<TC>& r, int t0, int end,
+template <int TC, int NS, bool F8, class Lim = WindowTokens>
+__device__ __forceinline__ void compute_tile(const KVTile<TC, F8>& r, int t0, int end,
                                              const bf16x8_t (&qop)[NS][4], float scale_log2e,
                                              const TileCtx& ctx, MfmaState<NS>& st,
                                              const Lim& lim = Lim{}) {
@@ -287,6 +361,14 @@ __device__ __forceinline__ void compute_tile(const KVTile<TC>& r, int t0, int en
   tile_scores<TC, NS>(r, t0, end, qop, scale_log2e, ctx, x, mt, lim);
 #pragma unroll
   for (int n = 0; n < NS; ++n) alpha[n] = softmax_update<TC>(x[n], mt[n], st.m[n], st.l[n]);
+  if constexpr (F8) {  // dequantised V = scale * code value: scale the probabilities (not l)
+#pragma unroll
+    for (int n = 0; n < NS; ++n)
+#pragma unroll
+      for (int c = 0; c < TC; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[n][c][i] *= r.vs[c];
+  }
   // out^T[d][col] += sum_t V[t][d] P[t][col] with v_mfma_f32_16x16x16_bf16, 16
   // dims per tile.  B = P: lane (col, qr) already holds P[4 qr + i][col].  p is
   // split into bf16 hi + lo (the top 8 and the next 8 mantissa bits), two
@@ -301,7 +383,7 @@ __device__ __forceinline__ void compute_tile(const KVTile<TC>& r, int t0, int en
 #pragma unroll
   for (int c = 0; c < TC; ++c) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ctx.v_lds[(4 * qr + i) * kKRowPad + ctx.col] = r.v[c][i];
+    for (int i = 0; i < 4; ++i) ctx.v_lds[(4 * qr + i) * kKRowPad + ctx.col] = r.vrow(c, i);
     bf16x4_t phi[NS], plo[NS];
 #pragma unroll
     for (int n = 0; n < NS; ++n) {
@@ -335,14 +417,20 @@ __device__ __forceinline__ void compute_tile(const KVTile<TC>& r, int t0, int en
 }
 
 // The same with P.V on the vector ALUs in fp32 (one column set, G heads).
-template <int TC, int G>
-__device__ __forceinline__ void compute_tile(const KVTile<TC>& r, int t0, int end,
+template <int TC, int G, bool F8>
+__device__ __forceinline__ void compute_tile(const KVTile<TC, F8>& r, int t0, int end,
                                              const bf16x8_t (&qop)[1][4], float scale_log2e,
                                              const TileCtx& ctx, ValuState<G>& st,
                                              const WindowTokens& = WindowTokens{}) {
   float x[1][TC][4], mt[1];
   tile_scores<TC, 1>(r, t0, end, qop, scale_log2e, ctx, x, mt);
   const float alpha = softmax_update<TC>(x[0], mt[0], st.m[0], st.l[0]);
+  if constexpr (F8) {  // each lane scales its own tokens' probabilities before they rotate
+#pragma unroll
+    for (int c = 0; c < TC; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[0][c][i] *= r.vs[c];
+  }
   static_for<G>([&](auto rr) {
     constexpr int R = decltype(rr)::value;
     const float ar = row_ror<R>(alpha);
@@ -354,7 +442,7 @@ __device__ __forceinline__ void compute_tile(const KVTile<TC>& r, int t0, int en
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float vf[8];
-      unpack_bf16x8(r.v[c][i], vf);
+      unpack_bf16x8(r.vrow(c, i), vf);
       static_for<G>([&](auto rr) {
         constexpr int R = decltype(rr)::value;
         const float pr = row_ror<R>(x[0][c][i]);
@@ -388,21 +476,18 @@ __device__ __forceinline__ void load_query(const DecodeArgs& a, int b, int kvh, 
 // makes the wave wait for those loads at the end of every iteration.  The
 // scheduling barriers keep the loads ahead of the compute.  Past the window's
 // end the loads re-read its last chunk (or the query row) and are never used.
-template <int BS, int TC, int NS, class State, class Lim = WindowTokens>
+template <int BS, int TC, bool F8, int NS, class State, class Lim = WindowTokens>
 __device__ __forceinline__ void stream_window(const DecodeArgs& a, const TileCtx& c, int begin,
                                               const bf16x8_t (&qop)[NS][4], State& st,
                                               const Lim& lim = Lim{}) {
   constexpr int TILE = 16 * TC;
   int t0 = begin;
-  KVTile<TC> ta, tb;
+  KVTile<TC, F8> ta, tb;
   load_tile<BS, TC>(ta, t0, c);
   // The first tile passes through an empty asm so that ta is not a load on
   // both incoming edges of the loop: otherwise the optimiser merges the two
   // loads of ta into one at the loop top, which undoes the prefetch.
-#pragma unroll
-  for (int ch = 0; ch < TC; ++ch)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(ta.k[ch][s]), "+v"(ta.v[ch][s]));
+  ta.pin();
   while (true) {
     load_tile<BS, TC>(tb, t0 + TILE, c);
     __builtin_amdgcn_sched_barrier(0);
@@ -431,7 +516,8 @@ struct TableCheck {
 // all waves.  `qrow` is a 256-byte row of this wave's queries: the target of
 // the prefetch past the end, which is never used.  Every thread of the
 // workgroup calls this with the same range.
-template <int BS, int TC, bool kCheck, int NS, class State, class Lim = WindowTokens>
+template <int BS, int TC, bool kCheck, bool F8 = false, int NS, class State,
+          class Lim = WindowTokens>
 __device__ __forceinline__ void attend_table(const DecodeArgs& a, int* s_bt, u32x4_t* k_lds,
                                              u32x4_t* v_lds, const int32_t* bt,
                                              const uint16_t* qrow, int kvh, int begin, int end,
@@ -456,6 +542,13 @@ __device__ __forceinline__ void attend_table(const DecodeArgs& a, int* s_bt, u32
   c.vdead = qrow + 8 * c.col;
   c.v_lds = v_lds;
   c.s_bt = s_bt;
+  if constexpr (F8) {
+    c.kbase8 = static_cast<const uint8_t*>(a.k_cache) + (int64_t)kvh * kD + 8 * c.col;
+    c.vbase8 = static_cast<const uint8_t*>(a.v_cache) + (int64_t)kvh * kD + 8 * c.col;
+    c.kscale = a.k_scale + kvh;
+    c.vscale = a.v_scale + kvh;
+    c.scale_stride = a.num_kv_heads;
+  }
   for (int w0 = begin; w0 < end; w0 += kMaxPartitionTokens) {
     const int wend = min(end, w0 + kMaxPartitionTokens);
     const int blk0 = w0 / BS;
@@ -477,19 +570,19 @@ __device__ __forceinline__ void attend_table(const DecodeArgs& a, int* s_bt, u32
     c.blk0 = blk0;
     c.end = wend;
     c.last_chunk = ((wend - 1) >> 4) << 4;
-    stream_window<BS, TC>(a, c, w0, qop, st, lim);
+    stream_window<BS, TC, F8>(a, c, w0, qop, st, lim);
   }
 }
 
 // attend_table over sequence b's own block table and queries.
-template <int G, int BS, int TC>
+template <int G, int BS, int TC, bool F8 = false>
 __device__ __forceinline__ void attend_range(const DecodeArgs& a, int* s_bt, u32x4_t* k_lds,
                                              u32x4_t* v_lds, int b, int kvh, int begin, int end,
                                              const bf16x8_t (&qop)[1][4], WaveState<G>& st) {
   const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
   const uint16_t* qrow =
       static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.num_q_heads + kvh * G) * kD;
-  attend_table<BS, TC, false>(a, s_bt, k_lds, v_lds, bt, qrow, kvh, begin, end, qop, st);
+  attend_table<BS, TC, false, F8>(a, s_bt, k_lds, v_lds, bt, qrow, kvh, begin, end, qop, st);
 }
 
 // Where a wave's finished range goes.

@@ -16,6 +16,7 @@ enum : unsigned {
   kErrCopyPair = 8u,   // copy src/dst outside [0, num_blocks)
   kErrShared = 16u,    // shared-prefix description disagrees with the tables or lengths
   kErrQuery = 32u,     // prefill query range out of order, past num_tokens or longer than seq_len
+  kErrScale = 64u,     // FP8 block scale not a positive finite number
 };
 
 constexpr int kDefaultPartitionTokens = 512;
@@ -81,6 +82,8 @@ struct DecodeArgs {
   int32_t out_bf16;
   int32_t slices;      // > 0: balanced schedule with this many slices per kv head
   float scale_log2e;   // softmax scale * log2(e): scores feed exp2
+  const float* k_scale;  // FP8 pools: per (block, kv head) scales, [num_blocks][num_kv_heads]
+  const float* v_scale;
 };
 
 // Workspace carve-up shared by the size query and the launch.
@@ -98,20 +101,39 @@ hipError_t launch_kv_write(const void* k, const void* v, const int64_t* slots, i
 // Whole-block copies from the (src_k, src_v) pools to the (dst_k, dst_v)
 // pools, which may be the same pools (copy-on-write) or different ones
 // (swapping); every pointer must be addressable by the device.
+// Scales (FP8 pools): when src_ks is non-null, each pair also copies the
+// `scales` K and V scales of its block (src_ks/src_vs -> dst_ks/dst_vs).
+struct BlockScales {
+  float* dst_ks = nullptr;
+  float* dst_vs = nullptr;
+  const float* src_ks = nullptr;
+  const float* src_vs = nullptr;
+  int scales = 0;
+};
 hipError_t launch_block_copy(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
                              const int64_t* pairs, int64_t num_pairs, int64_t src_blocks,
                              int64_t dst_blocks, int64_t block_bytes, unsigned* err,
-                             hipStream_t stream);
+                             hipStream_t stream, const BlockScales& sc = BlockScales{});
 
 // Chooses the kernel for (dtype, head_dim, block_size, group) and schedule
 // (a.slices > 0: balanced; else the partition grid) and launches the main
 // pass and, when partial results can exist, the matching reduce.  Returns
-// hipErrorInvalidValue for a combination that has no kernel.
+// hipErrorInvalidValue for a combination that has no kernel.  fp8: the pools
+// hold E4M3 codes with the per-block scales a.k_scale / a.v_scale.
 hipError_t launch_decode(const DecodeArgs& a, int bf16, int head_dim, int block_size, int group,
-                         hipStream_t stream);
+                         hipStream_t stream, bool fp8 = false);
 
-// The bf16 head_dim-128 kernels of either schedule (attention_mfma.hip).
-hipError_t launch_mfma_decode(const DecodeArgs& a, int block_size, int group, hipStream_t stream);
+// The head_dim-128 matrix-core kernels of either schedule (attention_mfma.hip),
+// bf16 pools or (fp8 set) E4M3 pools with a.k_scale / a.v_scale.
+hipError_t launch_mfma_decode(const DecodeArgs& a, int block_size, int group, hipStream_t stream,
+                              bool fp8 = false);
+
+// Slot-mapping write into E4M3 pools (kv_write.hip): bf16 rows in, each element
+// divided by its block's scale and rounded to the nearest code.
+hipError_t launch_kv_write_fp8(const void* k, const void* v, const int64_t* slots, int64_t n,
+                               void* k_cache, void* v_cache, const float* k_scale,
+                               const float* v_scale, int64_t num_slots, int block_size,
+                               int num_kv_heads, int head_dim, unsigned* err, hipStream_t stream);
 
 // Decode with shared prefixes (attention_shared.hip).  A prefix stream reads
 // a group's shared blocks once for up to 16 * kSharedSets query columns, i.e.

@@ -27,16 +27,24 @@ __all__ = [
     "pkv_attention_shared_workspace_bytes",
     "pkv_attention_decode_shared",
     "pkv_attention_prefill",
+    "pkv_kv_write_fp8",
+    "pkv_attention_decode_fp8",
+    "pkv_block_copy_fp8",
+    "pkv_block_transfer_fp8",
     "pkv_check_device_errors",
     "pkv_last_error",
     "PKV_F32",
     "PKV_BF16",
+    "PKV_FP8_E4M3",
 ]
 
-PKV_F32, PKV_BF16 = 0, 1
+PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
 _STATUS = {0: "PKV_OK", -1: "PKV_ERR_INVALID_ARG", -2: "PKV_ERR_UNSUPPORTED",
            -3: "PKV_ERR_WORKSPACE", -4: "PKV_ERR_HIP"}
 _DTYPES = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}
+# FP8 pools hold E4M3 codes: uint8 tensors, or torch's float8_e4m3fn (the same
+# OCP encoding).
+_FP8_DTYPES = tuple(d for d in (torch.uint8, getattr(torch, "float8_e4m3fn", None)) if d is not None)
 
 
 class PagedKVError(RuntimeError):
@@ -84,10 +92,16 @@ def load_library() -> ctypes.CDLL:
                                                 ctypes.c_float, P, P, P, I32, P, SZ, P]
     lib.pkv_attention_prefill.argtypes = [P, I32, P, I64, P, P, P, D, P, I32, P, I32, I32,
                                           ctypes.c_float, P]
+    lib.pkv_kv_write_fp8.argtypes = [P, P, P, I64, P, P, P, P, D, P]
+    lib.pkv_attention_decode_fp8.argtypes = [P, I32, P, P, P, P, P, D, P, I32, P, I32, I32,
+                                             ctypes.c_float, I32, P, SZ, P]
+    lib.pkv_block_copy_fp8.argtypes = [P, P, P, P, D, P, I64, P]
+    lib.pkv_block_transfer_fp8.argtypes = [P, P, P, P, D, P, P, P, P, D, P, I64, P]
     lib.pkv_last_error.restype = ctypes.c_char_p
     lib.pkv_check_device_errors.argtypes = [P]
     for name in ("pkv_kv_write", "pkv_block_copy", "pkv_block_transfer", "pkv_attention_decode",
-                 "pkv_attention_decode_shared", "pkv_attention_prefill",
+                 "pkv_attention_decode_shared", "pkv_attention_prefill", "pkv_kv_write_fp8",
+                 "pkv_attention_decode_fp8", "pkv_block_copy_fp8", "pkv_block_transfer_fp8",
                  "pkv_check_device_errors"):
         getattr(lib, name).restype = ctypes.c_int
     _LIB = lib
@@ -143,6 +157,23 @@ def _desc(k_cache: torch.Tensor, v_cache: torch.Tensor, host_ok: bool = False) -
     return CacheDesc(nb, bs, hkv, d, _DTYPES[k_cache.dtype])
 
 
+def _desc_fp8(k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: torch.Tensor,
+              v_scale: torch.Tensor, host_ok: bool = False) -> CacheDesc:
+    """Descriptor of FP8 pools; checks the scales are fp32 ``[num_blocks, num_kv_heads]``."""
+    _need(k_cache, "k_cache", ndim=4, host_ok=host_ok)
+    _need(v_cache, "v_cache", dtype=k_cache.dtype, ndim=4, host_ok=host_ok)
+    if k_cache.dtype not in _FP8_DTYPES:
+        raise TypeError(f"FP8 pools must be uint8 or float8_e4m3fn, got {k_cache.dtype}")
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    nb, bs, hkv, d = k_cache.shape
+    for t, name in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        _need(t, name, dtype=torch.float32, ndim=2, host_ok=host_ok)
+        if tuple(t.shape) != (nb, hkv):
+            raise ValueError(f"{name} must be [{nb}, {hkv}], got {tuple(t.shape)}")
+    return CacheDesc(nb, bs, hkv, d, PKV_FP8_E4M3)
+
+
 def pkv_kv_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
                  k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
     """Scatter ``k``/``v`` ``[N, Hkv, D]`` into the pools at ``slot_mapping`` (int64, -1 skips)."""
@@ -189,8 +220,14 @@ def pkv_block_transfer(dst_k: torch.Tensor, dst_v: torch.Tensor, src_k: torch.Te
 def pkv_attention_workspace_bytes(k_cache: torch.Tensor, v_cache: torch.Tensor, num_seqs: int,
                                   num_q_heads: int, max_blocks_per_seq: int,
                                   partition_tokens: int = 0) -> int:
-    """Workspace bytes ``pkv_attention_decode`` needs for these pools and sizes."""
-    desc = _desc(k_cache, v_cache)
+    """Workspace bytes ``pkv_attention_decode`` (or, for FP8 pools,
+    ``pkv_attention_decode_fp8``) needs for these pools and sizes."""
+    if k_cache.dtype in _FP8_DTYPES:
+        _need(k_cache, "k_cache", ndim=4)
+        nb, bs, hkv, d = k_cache.shape
+        desc = CacheDesc(nb, bs, hkv, d, PKV_FP8_E4M3)
+    else:
+        desc = _desc(k_cache, v_cache)
     return int(load_library().pkv_attention_workspace_bytes(
         ctypes.byref(desc), num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens))
 
@@ -319,6 +356,83 @@ def pkv_attention_prefill(out: torch.Tensor, q: torch.Tensor, query_start: torch
         ctypes.byref(desc), _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), B, Hq,
         float(scale), _stream()))
     return out
+
+
+def pkv_kv_write_fp8(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                     k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: torch.Tensor,
+                     v_scale: torch.Tensor) -> None:
+    """Encode bf16 ``k``/``v`` ``[N, Hkv, D]`` into FP8 pools at ``slot_mapping`` with the blocks' scales."""
+    desc = _desc_fp8(k_cache, v_cache, k_scale, v_scale)
+    _need(k, "k", dtype=torch.bfloat16, ndim=3)
+    _need(v, "v", dtype=torch.bfloat16, ndim=3)
+    _need(slot_mapping, "slot_mapping", dtype=torch.int64, ndim=1)
+    n = slot_mapping.shape[0]
+    if tuple(k.shape) != (n, desc.num_kv_heads, desc.head_dim) or v.shape != k.shape:
+        raise ValueError(f"k/v must be [{n}, {desc.num_kv_heads}, {desc.head_dim}]")
+    _check(load_library().pkv_kv_write_fp8(_ptr(k), _ptr(v), _ptr(slot_mapping), n, _ptr(k_cache),
+                                           _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                           ctypes.byref(desc), _stream()))
+
+
+def pkv_attention_decode_fp8(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                             v_cache: torch.Tensor, k_scale: torch.Tensor, v_scale: torch.Tensor,
+                             block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                             partition_tokens: int = 0,
+                             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode attention over FP8 pools into ``out`` ``[B, Hq, 128]``; ``q`` is bf16.  Returns ``out``."""
+    desc = _desc_fp8(k_cache, v_cache, k_scale, v_scale)
+    _need(q, "q", dtype=torch.bfloat16, ndim=3)
+    _need(out, "out", ndim=3)
+    if out.dtype not in _DTYPES:
+        raise TypeError("out must be float32 or bfloat16")
+    _need(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _need(seq_lens, "seq_lens", dtype=torch.int32, ndim=1)
+    B, Hq, D = q.shape
+    if tuple(out.shape) != (B, Hq, D) or D != desc.head_dim:
+        raise ValueError("out/q shapes do not match [B, Hq, head_dim]")
+    if block_tables.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("block_tables/seq_lens must have B rows")
+    mb = block_tables.shape[1]
+    need = int(load_library().pkv_attention_workspace_bytes(
+        ctypes.byref(desc), B, Hq, mb, partition_tokens))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _need(workspace, "workspace")
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load_library().pkv_attention_decode_fp8(
+        _ptr(out), _DTYPES[out.dtype], _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+        _ptr(v_scale), ctypes.byref(desc), _ptr(block_tables), mb, _ptr(seq_lens), B, Hq,
+        float(scale), partition_tokens, _ptr(workspace), wbytes, _stream()))
+    return out
+
+
+def pkv_block_copy_fp8(k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: torch.Tensor,
+                       v_scale: torch.Tensor, src_dst_pairs: torch.Tensor) -> None:
+    """``pkv_block_copy`` for FP8 pools: codes and the blocks' scales move together."""
+    desc = _desc_fp8(k_cache, v_cache, k_scale, v_scale)
+    _need(src_dst_pairs, "src_dst_pairs", dtype=torch.int64, ndim=2)
+    if src_dst_pairs.shape[1] != 2:
+        raise ValueError("src_dst_pairs must be [n, 2]")
+    _check(load_library().pkv_block_copy_fp8(
+        _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), ctypes.byref(desc),
+        _ptr(src_dst_pairs), src_dst_pairs.shape[0], _stream()))
+
+
+def pkv_block_transfer_fp8(dst_k: torch.Tensor, dst_v: torch.Tensor, dst_k_scale: torch.Tensor,
+                           dst_v_scale: torch.Tensor, src_k: torch.Tensor, src_v: torch.Tensor,
+                           src_k_scale: torch.Tensor, src_v_scale: torch.Tensor,
+                           src_dst_pairs: torch.Tensor) -> None:
+    """``pkv_block_transfer`` for FP8 pools (either side may be pinned host memory)."""
+    dd = _desc_fp8(dst_k, dst_v, dst_k_scale, dst_v_scale, host_ok=True)
+    sd = _desc_fp8(src_k, src_v, src_k_scale, src_v_scale, host_ok=True)
+    _need(src_dst_pairs, "src_dst_pairs", dtype=torch.int64, ndim=2)
+    if src_dst_pairs.shape[1] != 2:
+        raise ValueError("src_dst_pairs must be [n, 2]")
+    _check(load_library().pkv_block_transfer_fp8(
+        _ptr(dst_k), _ptr(dst_v), _ptr(dst_k_scale), _ptr(dst_v_scale), ctypes.byref(dd),
+        _ptr(src_k), _ptr(src_v), _ptr(src_k_scale), _ptr(src_v_scale), ctypes.byref(sd),
+        _ptr(src_dst_pairs), src_dst_pairs.shape[0], _stream()))
 
 
 def pkv_check_device_errors() -> None:

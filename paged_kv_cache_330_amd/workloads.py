@@ -27,6 +27,12 @@ Recipe (numpy ``default_rng(seed)``, draws in this order): lengths; the free
 order of the pool (a permutation); q; K; V; the outlier mask.  Values are
 binary32 normal draws rounded to bfloat16 with round-to-nearest-even for the
 bf16 workloads.  Pool size is ceil(1.1 * blocks needed) unless fixed.
+
+FP8 pools take the same tokens; their per-(block, kv head) scales follow the
+usual max-abs calibration (``fp8_block_scales``): the largest magnitude among
+the tokens a block will hold, divided by 448 (the largest E4M3 value), so
+that no element saturates.  The scales are inputs of the write, chosen here
+as a caller would choose them.
 """
 from __future__ import annotations
 
@@ -45,6 +51,7 @@ __all__ = [
     "make_decode_workload",
     "PrefixSharingWorkload",
     "PrefillWorkload",
+    "fp8_block_scales",
 ]
 
 
@@ -131,6 +138,29 @@ def _draw_lengths(spec: ConfigSpec, rng, num_seqs: int) -> np.ndarray:
     raise ValueError(spec.lengths)
 
 
+def fp8_block_scales(k, v, slots, num_blocks: int, block_size: int, unused=np.nan):
+    """Per-(block, kv head) fp32 scales of an FP8 pool for the bf16 tokens
+    ``k``/``v`` ``[N, Hkv, D]`` written to ``slots`` ``[N]`` (-1: not written):
+    max |x| over the block's tokens of that head / 448, 1.0 where that max is 0,
+    ``unused`` for blocks that receive no token.  Returns (k_scale, v_scale),
+    each ``[num_blocks, Hkv]`` float32.  Input preparation only.
+    """
+    slots = np.asarray(slots, dtype=np.int64)
+    Hkv = k.shape[1]
+    res = []
+    for x in (k, v):
+        amax = np.full((num_blocks, Hkv), -1.0, np.float32)
+        for s in range(0, len(slots), 1 << 14):
+            part = np.ascontiguousarray(x[s:s + (1 << 14)])
+            mag = np.abs((part.astype(np.uint32) << np.uint32(16)).view(np.float32)).max(axis=2)
+            sl = slots[s:s + (1 << 14)]
+            ok = sl >= 0
+            np.maximum.at(amax, sl[ok] // block_size, mag[ok])
+        sc = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0))
+        res.append(np.where(amax < 0, np.float32(unused), sc).astype(np.float32))
+    return res[0], res[1]
+
+
 @dataclass
 class DecodeWorkload:
     """One decode step: prefill state, the step's writes, then attention.
@@ -189,6 +219,18 @@ class DecodeWorkload:
             return np.full(shape, val, np.float32), np.full(shape, val, np.float32)
         val = 0x7FC0 if fill == "nan" else 0
         return np.full(shape, val, np.uint16), np.full(shape, val, np.uint16)
+
+    def slot_of_row(self) -> np.ndarray:
+        """Slot of every token row (prefill and step), int64 ``[T]``."""
+        out = np.full(self.k_tokens.shape[0], -1, np.int64)
+        out[self.prefill_rows] = self.prefill_slots
+        out[self.step_rows] = self.step_slots
+        return out
+
+    def fp8_scales(self, unused=np.nan):
+        """``fp8_block_scales`` of this workload's tokens (bf16 workloads)."""
+        return fp8_block_scales(self.k_tokens, self.v_tokens, self.slot_of_row(), self.num_blocks,
+                                self.block_size, unused)
 
     def kv_bytes(self) -> int:
         """K+V bytes the decode step must read: sum_b L_b * Hkv * D * 2 * elem."""

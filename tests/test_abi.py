@@ -281,3 +281,70 @@ def test_prefill_validation(lib):
     assert prefill(lib, q=P(FAKE + 8)) == INVALID
     assert prefill(lib, scale=float("nan")) == INVALID
     assert prefill(lib, mb=0) == INVALID
+
+
+FP8 = 2
+
+
+def decode_fp8(lib, **kw):
+    a = dict(out=P(), out_dtype=0, q=P(), k=P(), v=P(), ks=P(), vs=P(), desc=desc(dtype=FP8),
+             bt=P(), mb=32, sl=P(), B=4, Hq=32, scale=0.088, part=0, ws=P(), wsb=1 << 30)
+    a.update(kw)
+    return lib.pkv_attention_decode_fp8(a["out"], a["out_dtype"], a["q"], a["k"], a["v"], a["ks"],
+                                        a["vs"], ctypes.byref(a["desc"]), a["bt"], a["mb"], a["sl"],
+                                        a["B"], a["Hq"], a["scale"], a["part"], a["ws"], a["wsb"],
+                                        P(0))
+
+
+def test_fp8_pools_only_through_fp8_calls(lib):
+    d8, d16 = desc(dtype=FP8), desc()
+    assert lib.pkv_kv_write(P(), P(), P(), 4, P(), P(), ctypes.byref(d8), P(0)) == UNSUPPORTED
+    assert "pkv_kv_write_fp8" in ops.pkv_last_error()
+    assert lib.pkv_block_copy(P(), P(), ctypes.byref(d8), P(), 1, P(0)) == UNSUPPORTED
+    assert lib.pkv_block_transfer(P(), P(), ctypes.byref(d8), P(), P(), ctypes.byref(d8), P(), 1,
+                                  P(0)) == UNSUPPORTED
+    assert decode(lib, desc=d8) == UNSUPPORTED
+    assert "pkv_attention_decode_fp8" in ops.pkv_last_error()
+    # and the FP8 calls take nothing else
+    assert lib.pkv_kv_write_fp8(P(), P(), P(), 4, P(), P(), P(), P(), ctypes.byref(d16),
+                                P(0)) == UNSUPPORTED
+    assert decode_fp8(lib, desc=d16) == UNSUPPORTED
+    assert lib.pkv_block_copy_fp8(P(), P(), P(), P(), ctypes.byref(d16), P(), 1, P(0)) == UNSUPPORTED
+
+
+def test_fp8_validation(lib):
+    d = desc(dtype=FP8)
+    # no-ops
+    assert lib.pkv_kv_write_fp8(P(0), P(0), P(0), 0, P(0), P(0), P(0), P(0), ctypes.byref(d),
+                                P(0)) == OK
+    assert lib.pkv_block_copy_fp8(P(0), P(0), P(0), P(0), ctypes.byref(d), P(0), 0, P(0)) == OK
+    assert decode_fp8(lib, B=0, out=P(0), q=P(0)) == OK
+    # scales are required and 4-byte aligned
+    assert lib.pkv_kv_write_fp8(P(), P(), P(), 4, P(), P(), P(0), P(), ctypes.byref(d),
+                                P(0)) == INVALID
+    assert "k_scale is NULL" in ops.pkv_last_error()
+    assert lib.pkv_kv_write_fp8(P(), P(), P(), 4, P(), P(), P(), P(FAKE + 2), ctypes.byref(d),
+                                P(0)) == INVALID
+    assert "v_scale" in ops.pkv_last_error()
+    assert decode_fp8(lib, ks=P(0)) == INVALID
+    assert "k_scale" in ops.pkv_last_error()
+    assert lib.pkv_block_copy_fp8(P(), P(), P(), P(0), ctypes.byref(d), P(), 1, P(0)) == INVALID
+    # FP8 attention runs on the head_dim 128 matrix-core kernels only
+    assert decode_fp8(lib, desc=desc(d=64, dtype=FP8)) == UNSUPPORTED
+    assert decode_fp8(lib, Hq=24) == UNSUPPORTED
+    assert decode_fp8(lib, scale=float("nan")) == INVALID
+    # transfer pools must agree in shape and dtype
+    other = desc(bs=32, dtype=FP8)
+    assert lib.pkv_block_transfer_fp8(P(), P(), P(), P(), ctypes.byref(other), P(), P(), P(), P(),
+                                      ctypes.byref(d), P(), 1, P(0)) == INVALID
+    assert lib.pkv_block_transfer_fp8(P(), P(), P(), P(), ctypes.byref(desc()), P(), P(), P(), P(),
+                                      ctypes.byref(d), P(), 1, P(0)) == INVALID
+
+
+def test_fp8_workspace_matches_bf16(lib):
+    # FP8 decode uses the same schedules, hence the same workspace, as bf16
+    for B, part in ((256, 0), (4, 0), (4, 512), (3000, 0)):
+        w16 = lib.pkv_attention_workspace_bytes(ctypes.byref(desc()), B, 32, 256, part)
+        w8 = lib.pkv_attention_workspace_bytes(ctypes.byref(desc(dtype=FP8)), B, 32, 256, part)
+        assert w8 == w16 > 0, (B, part, w8, w16)
+    assert decode_fp8(lib, ws=P(0)) == WORKSPACE
