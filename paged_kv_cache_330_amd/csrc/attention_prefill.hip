@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void prefill_kernel(PrefillArgs pa)
   const DecodeArgs& a = pa.d;
   __shared__ int s_bt[kMaxPartitionTokens / BS + 1];
   __shared__ u32x4_t s_kt[kMaxWaves * 16 * kKRowPad];
-  __shared__ u32x4_t s_vt[kMaxWaves * 16 * kKRowPad];
+  __shared__ u32x4_t s_vt[kMaxWaves * 16 * kVRowPad];
   __shared__ int s_item[kMaxBalancedSeqs + 1];  // first work item of each sequence
   __shared__ int s_wsum[kMaxWaves];
 
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void prefill_kernel(PrefillArgs pa)
   }
   MfmaState<kSharedSets> st;
   st.reset();
-  attend_table<BS, 1, false>(a, s_bt, s_kt + wave * 16 * kKRowPad, s_vt + wave * 16 * kKRowPad,
+  attend_table<BS, 1, false>(a, s_bt, s_kt + wave * 16 * kKRowPad, s_vt + wave * 16 * kVRowPad,
                              a.block_tables + (int64_t)b * a.max_blocks_per_seq,
                              q + ((int64_t)r0 * a.num_q_heads + kvh * G) * kD, kvh, 0, pos0 + t1,
                              qop, st, TableCheck{nullptr, 0}, lim);

@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_shared_kernel(SharedArg
   const DecodeArgs& a = sa.d;
   __shared__ int s_bt[kMaxPartitionTokens / BS + 1];
   __shared__ u32x4_t s_kt[PKV_K_VIA_LDS ? kMaxWaves * 16 * kKRowPad : 1];
-  __shared__ u32x4_t s_vt[kMaxWaves * 16 * kKRowPad];  // prefix pieces: P.V on the matrix cores
+  __shared__ u32x4_t s_vt[kMaxWaves * 16 * kVRowPad];  // prefix pieces: P.V on the matrix cores
   __shared__ int s_goff[kMaxBalancedSeqs + 1];  // member offsets of the groups
   __shared__ int s_gsp[kMaxBalancedSeqs + 1];   // first prefix stream of each group
   __shared__ int s_midx[kMaxBalancedSeqs];      // member index of each sequence, or -1
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_shared_kernel(SharedArg
   const bool reporter = blockIdx.x == 0 && slice == 0;
   const int cap = a.max_blocks_per_seq * BS;
   u32x4_t* k_lds = s_kt + (PKV_K_VIA_LDS ? wave * 16 * kKRowPad : 0);
-  u32x4_t* v_lds = s_vt + wave * 16 * kKRowPad;
+  u32x4_t* v_lds = s_vt + wave * 16 * kVRowPad;
 
   // 1. One round of independent global loads: group offsets, shared lengths,
   //    sequence lengths.  Offsets must start at 0, not decrease and stay

@@ -123,6 +123,23 @@ struct KVTile<TC, true> {
 // column reads are free of bank conflicts.
 constexpr int kKRowPad = 17;  // 16-byte units per LDS row
 
+// The V tile of P.V on the matrix cores is read back with gfx950's
+// transposing LDS read (ds_read_b64_tr_b16): in each group of 16 lanes, lane
+// 4 a + c receives, as element i, the c-th 16-bit value of the 8 bytes
+// addressed by lane a + 4 i of the group.  Lane (col, qr) addresses row
+// 4 qr + col / 4, dims 16 j + 4 (col % 4) .. + 3, so it receives
+// V[4 qr + i][16 j + col], i = 0..3: the A operand of one 16x16x16 product in
+// one instruction (instead of four 16-bit reads).  Rows are padded to 18
+// 16-byte units, which puts the 8 rows a 32-lane half reads on 8 distinct
+// 8-bank groups.
+constexpr int kVRowPad = PKV_V_TR_READ ? 18 : kKRowPad;  // 16-byte units per V row
+
+__device__ __forceinline__ bf16x4_t lds_read_tr16(const uint16_t* p) {
+  typedef short v4i16_t __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(
+      bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)(p)));
+}
+
 struct TileCtx {
   const uint16_t* kbase;  // K pool + kv head offset + this lane's d-chunk (or dims)
   const uint16_t* vbase;  // V pool + kv head offset + this lane's dims
@@ -167,8 +184,13 @@ __device__ __forceinline__ u32x2_t load_kv8(const uint8_t* p) {
 // scores of such tokens are masked to -inf).  A chunk wholly past the end
 // (the prefetch after a window's last tile, never computed) reads this
 // wave's 256-byte query row instead, which is in cache, so it costs no HBM
-// traffic.  FP8 pools: a lane's 4 rows (4 qr .. 4 qr + 3, clamped to the
-// window's last token) always lie in one block, whose scales it loads too.
+// traffic.  (Skipping those loads behind a wave-uniform branch instead makes
+// the compiler wait for all outstanding loads before the next tile's, which
+// undoes the prefetch.)  FP8 pools: a lane's 4 rows (4 qr .. 4 qr + 3,
+// clamped to the window's last token) always lie in one block, whose scales
+// it loads too; a dead chunk re-reads the last chunk (its codes must decode
+// to finite values: with several chunks per tile a dead chunk is computed,
+// and its values are multiplied by zero probabilities).
 template <int BS, int TC, bool F8 = false>
 __device__ __forceinline__ void load_tile(KVTile<TC, F8>& r, int t0, const TileCtx& c) {
 #pragma unroll
@@ -194,15 +216,18 @@ __device__ __forceinline__ void load_tile(KVTile<TC, F8>& r, int t0, const TileC
       const int tv = min(tce + 4 * c.qr + i, c.end - 1);
       const int64_t row = ((int64_t)pv[i] * BS + (tv & (BS - 1))) * c.tok_stride;
       if constexpr (F8) {
-        r.k[ch][i] = load_kv8(dead ? reinterpret_cast<const uint8_t*>(c.kdead) : c.kbase8 + row);
-        r.v[ch][i] = load_kv8(dead ? reinterpret_cast<const uint8_t*>(c.vdead) : c.vbase8 + row);
+        r.k[ch][i] = load_kv8(c.kbase8 + row);
+        r.v[ch][i] = load_kv8(c.vbase8 + row);
+      } else if (TC == 1 && PKV_DEAD_REREAD) {
+        r.k[ch][i] = load_kv(c.kbase + row);
+        r.v[ch][i] = load_kv(c.vbase + row);
       } else {
         r.k[ch][i] = load_kv(dead ? c.kdead : c.kbase + row);
         r.v[ch][i] = load_kv(dead ? c.vdead : c.vbase + row);
       }
     }
     if constexpr (F8) {
-      const int64_t si = (int64_t)(dead ? 0 : pv[0]) * c.scale_stride;
+      const int64_t si = (int64_t)pv[0] * c.scale_stride;
       r.ks[ch] = c.kscale[si];
       r.vs[ch] = c.vscale[si];
     }
@@ -375,15 +400,23 @@ __device__ __forceinline__ void compute_tile(const KVTile<TC, F8>& r, int t0, in
   // products each, so p keeps 16 bits.  A = V^T: lane (col, qr) takes
   // V[4 qr + i][16 j + col], read column-wise from the V rows this wave wrote
   // to LDS; every column set uses the same A operand.
+  // Rescale the accumulators only when some column's running max moved
+  // (alpha == 1 exactly otherwise, so skipping changes no bit); past the
+  // first few hundred tokens most tiles skip it.
+  bool moved = false;
 #pragma unroll
-  for (int n = 0; n < NS; ++n)
+  for (int n = 0; n < NS; ++n) moved |= alpha[n] != 1.f;
+  if (!PKV_LAZY_RESCALE || __builtin_amdgcn_ballot_w64(moved) != 0) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) st.o[n][j] *= alpha[n];
+    for (int n = 0; n < NS; ++n)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) st.o[n][j] *= alpha[n];
+  }
   const uint16_t* vcol = reinterpret_cast<const uint16_t*>(ctx.v_lds);
 #pragma unroll
   for (int c = 0; c < TC; ++c) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ctx.v_lds[(4 * qr + i) * kKRowPad + ctx.col] = r.vrow(c, i);
+    for (int i = 0; i < 4; ++i) ctx.v_lds[(4 * qr + i) * kVRowPad + ctx.col] = r.vrow(c, i);
     bf16x4_t phi[NS], plo[NS];
 #pragma unroll
     for (int n = 0; n < NS; ++n) {
@@ -402,11 +435,16 @@ __device__ __forceinline__ void compute_tile(const KVTile<TC, F8>& r, int t0, in
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
+#if PKV_V_TR_READ
+      const bf16x4_t vt =
+          lds_read_tr16(vcol + (4 * qr + ctx.col / 4) * (kVRowPad * 8) + 16 * j + 4 * (ctx.col % 4));
+#else
       uint16_t e[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) e[t] = vcol[(4 * qr + t) * (kKRowPad * 8) + 16 * j + ctx.col];
+      for (int t = 0; t < 4; ++t) e[t] = vcol[(4 * qr + t) * (kVRowPad * 8) + 16 * j + ctx.col];
       const uint32_t va[2] = {e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16)};
       const bf16x4_t vt = __builtin_bit_cast(bf16x4_t, va);
+#endif
 #pragma unroll
       for (int n = 0; n < NS; ++n) {
         st.o[n][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, phi[n], st.o[n][j], 0, 0, 0);
@@ -500,6 +538,13 @@ __device__ __forceinline__ void stream_window(const DecodeArgs& a, const TileCtx
     t0 += TILE;
     if (t0 >= c.end) break;
   }
+#if PKV_DRAIN_PREFETCH
+  // Wait here for the prefetch past the end (vmcnt 0; expcnt and lgkmcnt
+  // left free).  Otherwise it is still in flight when the caller streams its
+  // next window, whose loop head is the same code, and the compiler puts a
+  // full wait at that head, in front of every other tile's loads.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+#endif
 }
 
 // Sequences whose block tables must agree with the streamed table over every

@@ -27,6 +27,21 @@ constexpr int kMaxBalancedSeqs = 2048;     // batch limit of the balanced schedu
 #ifndef PKV_MFMA_TILE_CHUNKS
 #define PKV_MFMA_TILE_CHUNKS 1  // 16-token chunks per wave tile
 #endif
+#ifndef PKV_FP8_TILE_CHUNKS
+#define PKV_FP8_TILE_CHUNKS 1  // the same for FP8 pools
+#endif
+#ifndef PKV_V_TR_READ
+#define PKV_V_TR_READ 1         // V^T operand of P.V read with ds_read_b64_tr_b16 (0: 16-bit reads)
+#endif
+#ifndef PKV_DEAD_REREAD
+#define PKV_DEAD_REREAD 1       // one chunk per tile: the prefetch past a window re-reads its last chunk
+#endif
+#ifndef PKV_DRAIN_PREFETCH
+#define PKV_DRAIN_PREFETCH 1    // drain the prefetch past a window's end before leaving it
+#endif
+#ifndef PKV_LAZY_RESCALE
+#define PKV_LAZY_RESCALE 1      // P.V accumulators rescaled only in tiles where a running max moved
+#endif
 #ifndef PKV_KV_NONTEMPORAL
 #define PKV_KV_NONTEMPORAL 1    // K/V loads carry the streaming hint (0: plain loads)
 #endif
