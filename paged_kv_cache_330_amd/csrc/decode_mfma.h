@@ -526,18 +526,20 @@ __device__ __forceinline__ void stream_window(const DecodeArgs& a, const TileCtx
   // both incoming edges of the loop: otherwise the optimiser merges the two
   // loads of ta into one at the loop top, which undoes the prefetch.
   ta.pin();
-  while (true) {
+  // Pairs of tiles with a single exit: with an exit after each half the
+  // compiler joins both exits in one block with an edge back to the loop
+  // head, and must then wait for every load at the head.
+  const int n = (c.end - begin + TILE - 1) / TILE;  // tiles of the window (uniform)
+  for (int i = 0; i + 1 < n; i += 2) {
     load_tile<BS, TC>(tb, t0 + TILE, c);
     __builtin_amdgcn_sched_barrier(0);
     compute_tile<TC>(ta, t0, c.end, qop, a.scale_log2e, c, st, lim);
-    t0 += TILE;
-    if (t0 >= c.end) break;
-    load_tile<BS, TC>(ta, t0 + TILE, c);
+    load_tile<BS, TC>(ta, t0 + 2 * TILE, c);
     __builtin_amdgcn_sched_barrier(0);
-    compute_tile<TC>(tb, t0, c.end, qop, a.scale_log2e, c, st, lim);
-    t0 += TILE;
-    if (t0 >= c.end) break;
+    compute_tile<TC>(tb, t0 + TILE, c.end, qop, a.scale_log2e, c, st, lim);
+    t0 += 2 * TILE;
   }
+  if (n & 1) compute_tile<TC>(ta, t0, c.end, qop, a.scale_log2e, c, st, lim);
 #if PKV_DRAIN_PREFETCH
   // Wait here for the prefetch past the end (vmcnt 0; expcnt and lgkmcnt
   // left free).  Otherwise it is still in flight when the caller streams its
