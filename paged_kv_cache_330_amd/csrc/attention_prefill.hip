@@ -10,17 +10,22 @@
 // tokens), and the token at position p attends to the cached tokens 0 .. p.
 // The decode step is the one-token case.
 //
-// Work split.  A work item is QT = 32 / G consecutive new tokens of one
-// sequence (grid x: work items, grid y: kv-head groups); its QT x G queries
-// fill the 32 columns of two 16-column MFMA sets (column 16 n + col: token
-// (16 n + col) / G of the item, head col % G), so
-// Q.K^T and P.V are dense products of each K/V tile with 32 queries.  A
-// workgroup has one wave per kv head and takes one item: its waves stream the
-// item's key range, tokens 0 .. (position of its last token), through the
-// block table, each column masking the tokens after its own position.  Items
-// are numbered sequence by sequence from the per-sequence counts (a prefix
-// scan in LDS) and dispatched from the last to the first, so the longest key
-// ranges of each sequence start early.
+// Work split.  A work item is QT = 4 x 32 / G consecutive new tokens of one
+// sequence and one kv head (grid x: work items, grid y: kv heads).  Its four
+// waves each take 32 / G of the tokens: their 32 x G queries fill the 32
+// columns of two 16-column MFMA sets (column 16 n + col: token
+// (16 n + col) / G of the wave, head col % G), so Q.K^T and P.V are dense
+// products of each K/V tile with 32 queries per wave.  The item streams its
+// key range, tokens 0 .. (position of its last token), through the block
+// table in 16-token tiles shared by the four waves: every lane loads one
+// 16-byte unit of a K row and of a V row into double-buffered LDS tiles (one
+// barrier per tile; the next tile's loads are in flight while the current one
+// is computed), and each wave reads its MFMA operands from there, masking the
+// tokens after its own columns' positions.  Sharing each tile between four
+// waves cuts the K/V reads per query four times against one wave per tile.
+// Items are numbered sequence by sequence from the per-sequence counts (a
+// prefix scan in LDS) and dispatched from the last to the first, so the
+// longest key ranges of each sequence start early.
 //
 // Checks: a query range with query_start[b] < 0, query_start[b + 1] <
 // query_start[b], query_start[b + 1] > num_tokens, or more new tokens than
@@ -30,23 +35,36 @@
 namespace pkv {
 namespace {
 
-constexpr int kCols = 16 * kSharedSets;  // query columns of a work item
+#ifndef PKV_PREFILL_CHUNKS
+#define PKV_PREFILL_CHUNKS 2  // 16-token chunks per shared K/V tile
+#endif
+#ifndef PKV_PREFILL_PV32
+#define PKV_PREFILL_PV32 1    // P.V of chunk pairs with the 16x16x32 product
+#endif
+
+constexpr int kCols = 16 * kSharedSets;  // query columns of a wave
+constexpr int kItemWaves = 4;            // waves of a work item, sharing each K/V tile
+constexpr int kItemThreads = kItemWaves * 64;
+constexpr int kTC = PKV_PREFILL_CHUNKS;  // chunks per tile
+constexpr int kTileRows = 16 * kTC;      // tokens per tile
+static_assert(kItemThreads == 16 * 16, "one 16-byte unit of 16 rows per lane and chunk");
 
 template <int G, int BS>
-__global__ __launch_bounds__(kMaxWaves * 64) void prefill_kernel(PrefillArgs pa) {
+__global__ __launch_bounds__(kItemThreads) void prefill_kernel(PrefillArgs pa) {
   static_assert(16 % G == 0, "group must divide 16");
-  constexpr int QT = kCols / G;  // new tokens per work item
+  constexpr int QW = kCols / G;         // new tokens per wave
+  constexpr int QT = kItemWaves * QW;   // new tokens per work item
   const DecodeArgs& a = pa.d;
   __shared__ int s_bt[kMaxPartitionTokens / BS + 1];
-  __shared__ u32x4_t s_kt[kMaxWaves * 16 * kKRowPad];
-  __shared__ u32x4_t s_vt[kMaxWaves * 16 * kVRowPad];
+  __shared__ u32x4_t s_k[2][kTileRows * kKRowPad];
+  __shared__ u32x4_t s_v[2][kTileRows * kVRowPad];
   __shared__ int s_item[kMaxBalancedSeqs + 1];  // first work item of each sequence
-  __shared__ int s_wsum[kMaxWaves];
+  __shared__ int s_wsum[kItemWaves];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int col = lane & 15, qr = lane >> 4;
-  const int kvh = blockIdx.y * (blockDim.x >> 6) + wave;
+  const int kvh = blockIdx.y;
   const int B = a.num_seqs;
   const bool reporter = blockIdx.x == 0 && blockIdx.y == 0;
   const int32_t* qs = pa.query_start;
@@ -72,7 +90,9 @@ __global__ __launch_bounds__(kMaxWaves * 64) void prefill_kernel(PrefillArgs pa)
   const int r0 = qs[b];
   const int pos0 = clamped_len(a, BS, b, false) - n;  // position of new token 0
   const int t0 = (item - s_item[b]) * QT;
-  const int t1 = min(n, t0 + QT);
+  const int t1 = min(n, t0 + QT);          // the item's new tokens [t0, t1)
+  const int wt0 = t0 + wave * QW;          // this wave's: [wt0, min(t1, wt0 + QW))
+  const int wt1 = min(t1, wt0 + QW);
 
   // Columns: query rows and causal limits (a column past the item's last
   // token repeats it; its output is not stored).
@@ -81,24 +101,97 @@ __global__ __launch_bounds__(kMaxWaves * 64) void prefill_kernel(PrefillArgs pa)
   CausalTokens<kSharedSets> lim;
 #pragma unroll
   for (int s = 0; s < kSharedSets; ++s) {
-    const int t = min(t0 + (16 * s + col) / G, t1 - 1);
+    const int t = min(wt0 + (16 * s + col) / G, t1 - 1);
     load_qop(q + ((int64_t)(r0 + t) * a.num_q_heads + kvh * G + col % G) * kD, qr, qop[s]);
     lim.limit[s] = pos0 + t + 1;
   }
   MfmaState<kSharedSets> st;
   st.reset();
-  attend_table<BS, 1, false>(a, s_bt, s_kt + wave * 16 * kKRowPad, s_vt + wave * 16 * kVRowPad,
-                             a.block_tables + (int64_t)b * a.max_blocks_per_seq,
-                             q + ((int64_t)r0 * a.num_q_heads + kvh * G) * kD, kvh, 0, pos0 + t1,
-                             qop, st, TableCheck{nullptr, 0}, lim);
 
-  // Normalised outputs of the item's columns.
+  // The lane's units of each tile: rows urow + 16 c, 16 bytes at dims 8 ucol ..
+  const int urow = threadIdx.x >> 4, ucol = threadIdx.x & 15;
+  const int64_t tok_stride = (int64_t)a.num_kv_heads * kD;
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k_cache) + (int64_t)kvh * kD + 8 * ucol;
+  const uint16_t* vbase = static_cast<const uint16_t*>(a.v_cache) + (int64_t)kvh * kD + 8 * ucol;
+  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
+  const int kend = pos0 + t1;  // key tokens of the item: 0 .. kend - 1
+  for (int w0 = 0; w0 < kend; w0 += kMaxPartitionTokens) {
+    const int wend = min(kend, w0 + kMaxPartitionTokens);
+    const int blk0 = w0 / BS;
+    const int nblk = (wend - 1) / BS - blk0 + 1;
+    __syncthreads();  // every wave is done with the previous window's ids and tiles
+    for (int i = threadIdx.x; i < nblk; i += blockDim.x)
+      s_bt[i] = checked_block(bt, blk0 + i, a.num_blocks, a.err);
+    __syncthreads();
+    // Rows past the window's end re-read its last token (masked).
+    u32x4_t rk[kTC], rv[kTC];
+    auto load_units = [&](int tt) {
+#pragma unroll
+      for (int c = 0; c < kTC; ++c) {
+        const int tok = min(tt + 16 * c + urow, wend - 1);
+        const int64_t row =
+            ((int64_t)s_bt[tok / BS - blk0] * BS + (tok & (BS - 1))) * tok_stride;
+        rk[c] = *reinterpret_cast<const u32x4_t*>(kbase + row);
+        rv[c] = *reinterpret_cast<const u32x4_t*>(vbase + row);
+      }
+    };
+    auto stage = [&](int buf) {
+#pragma unroll
+      for (int c = 0; c < kTC; ++c) {
+        s_k[buf][(16 * c + urow) * kKRowPad + ucol] = rk[c];
+        s_v[buf][(16 * c + urow) * kVRowPad + ucol] = rv[c];
+      }
+    };
+    load_units(w0);
+    stage(0);
+    const int ntile = (wend - w0 + kTileRows - 1) / kTileRows;
+    for (int i = 0; i < ntile; ++i) {
+      const int tt = w0 + kTileRows * i;
+      load_units(tt + kTileRows);  // next tile (past the end: re-reads, unused)
+      __syncthreads();             // tile i is in buffer i & 1; tile i - 1 is done
+      const u32x4_t* kt = s_k[i & 1];
+      float x[kSharedSets][kTC][4], mt[kSharedSets], alpha[kSharedSets];
+#pragma unroll
+      for (int m = 0; m < kSharedSets; ++m) mt[m] = -INFINITY;
+#pragma unroll
+      for (int c = 0; c < kTC; ++c) {
+        u32x4_t kop[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) kop[s] = kt[(16 * c + col) * kKRowPad + 4 * s + qr];
+        scores_from_kop<kTC, kSharedSets>(kop, c, tt + 16 * c, wend, qop, a.scale_log2e, qr, x,
+                                          mt, lim);
+      }
+      column_max<kSharedSets>(mt);
+#pragma unroll
+      for (int m = 0; m < kSharedSets; ++m)
+        alpha[m] = softmax_update<kTC>(x[m], mt[m], st.m[m], st.l[m]);
+      rescale_lazy<kSharedSets>(alpha, st);
+      const uint16_t* vt = reinterpret_cast<const uint16_t*>(s_v[i & 1]);
+#if PKV_PREFILL_PV32
+#pragma unroll
+      for (int c = 0; c + 1 < kTC; c += 2)
+        pv_pair_from_lds<kTC, kSharedSets>(vt + 16 * c * kVRowPad * 8,
+                                           vt + 16 * (c + 1) * kVRowPad * 8, c, c + 1, x, col,
+                                           qr, st);
+      if constexpr (kTC & 1)
+        pv_from_lds<kTC, kSharedSets>(vt + 16 * (kTC - 1) * kVRowPad * 8, kTC - 1, x, col, qr,
+                                      st);
+#else
+#pragma unroll
+      for (int c = 0; c < kTC; ++c)
+        pv_from_lds<kTC, kSharedSets>(vt + 16 * c * kVRowPad * 8, c, x, col, qr, st);
+#endif
+      stage((i + 1) & 1);  // tile i + 1
+    }
+  }
+
+  // Normalised outputs of the wave's columns.
 #pragma unroll
   for (int s = 0; s < kSharedSets; ++s) {
     st.l[s] += __shfl_xor(st.l[s], 16);
     st.l[s] += __shfl_xor(st.l[s], 32);
-    const int t = t0 + (16 * s + col) / G;
-    if (t < t1) {
+    const int t = wt0 + (16 * s + col) / G;
+    if (t < wt1) {
       const int64_t o = ((int64_t)(r0 + t) * a.num_q_heads + kvh * G + col % G) * kD + 4 * qr;
       const float inv = 1.f / st.l[s];
 #pragma unroll
@@ -110,12 +203,12 @@ __global__ __launch_bounds__(kMaxWaves * 64) void prefill_kernel(PrefillArgs pa)
 }
 
 template <int G>
-hipError_t launch_prefill_g(const PrefillArgs& a, int block_size, int kh, hipStream_t s) {
-  constexpr int QT = kCols / G;
+hipError_t launch_prefill_g(const PrefillArgs& a, int block_size, hipStream_t s) {
+  constexpr int QT = kItemWaves * kCols / G;
   // Work items: at most ceil(T / QT) + B when the query ranges are consistent.
   const int64_t items = (a.num_tokens + QT - 1) / QT + a.d.num_seqs;
-  const dim3 grid(static_cast<unsigned>(items), a.d.num_kv_heads / kh);
-  const dim3 block(kh * 64);
+  const dim3 grid(static_cast<unsigned>(items), a.d.num_kv_heads);
+  const dim3 block(kItemThreads);
   switch (block_size) {
     case 8: prefill_kernel<G, 8><<<grid, block, 0, s>>>(a); break;
     case 16: prefill_kernel<G, 16><<<grid, block, 0, s>>>(a); break;
@@ -130,14 +223,13 @@ hipError_t launch_prefill_g(const PrefillArgs& a, int block_size, int kh, hipStr
 
 hipError_t launch_prefill(const PrefillArgs& a, int block_size, int group, hipStream_t s) {
   if (a.d.num_seqs < 1 || a.d.num_seqs > kMaxBalancedSeqs || a.num_tokens < 1 ||
-      a.num_tokens > 0x7FFFFFFF)
+      a.num_tokens > 0x7FFFFFFF || a.d.num_kv_heads > 65535)
     return hipErrorInvalidValue;
-  const int kh = mfma_waves_per_group(a.d.num_kv_heads);
   switch (group) {
-    case 1: return launch_prefill_g<1>(a, block_size, kh, s);
-    case 2: return launch_prefill_g<2>(a, block_size, kh, s);
-    case 4: return launch_prefill_g<4>(a, block_size, kh, s);
-    case 8: return launch_prefill_g<8>(a, block_size, kh, s);
+    case 1: return launch_prefill_g<1>(a, block_size, s);
+    case 2: return launch_prefill_g<2>(a, block_size, s);
+    case 4: return launch_prefill_g<4>(a, block_size, s);
+    case 8: return launch_prefill_g<8>(a, block_size, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -305,6 +305,41 @@ struct CausalTokens {
   }
 };
 
+// Q.K^T of chunk c (tokens tok0 .. tok0 + 15) for NS sets of query columns
+// from the chunk's K operand (lane (col, qr): d-chunk 4 s + qr of row col),
+// scaled by sl; tokens a column does not attend to score -inf.  mt[n] takes
+// the maximum of set n over this lane's rows.
+template <int TC, int NS, class Lim>
+__device__ __forceinline__ void scores_from_kop(const u32x4_t (&kop)[4], int c, int tok0, int end,
+                                                const bf16x8_t (&qop)[NS][4], float sl, int qr,
+                                                float (&x)[NS][TC][4], float (&mt)[NS],
+                                                const Lim& lim) {
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop[s]),
+                                                      qop[n][s], sacc, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = tok0 + 4 * qr + i;
+      x[n][c][i] = lim.valid(n, tok, end) ? sacc[i] * sl : -INFINITY;
+      mt[n] = fmaxf(mt[n], x[n][c][i]);
+    }
+  }
+}
+
+// Column maxima over the four row groups of a wave.
+template <int NS>
+__device__ __forceinline__ void column_max(float (&mt)[NS]) {
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    mt[n] = fmaxf(mt[n], __shfl_xor(mt[n], 16));
+    mt[n] = fmaxf(mt[n], __shfl_xor(mt[n], 32));
+  }
+}
+
 // Q.K^T of one loaded tile for NS sets of query columns, scaled by
 // scale * log2(e); tokens the columns do not attend to (at or past `end`, or
 // past a column's limit) score -inf.  mt[n] is the tile's maximum of set n
@@ -330,28 +365,11 @@ __device__ __forceinline__ void tile_scores(const KVTile<TC, F8>& r, int t0, int
 #pragma unroll
     for (int s = 0; s < 4; ++s) kop[s] = r.krow(c, s);
 #endif
-#pragma unroll
-    for (int n = 0; n < NS; ++n) {
-      f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop[s]),
-                                                        qop[n][s], sacc, 0, 0, 0);
-      float sl = scale_log2e;
-      if constexpr (F8) sl *= r.ks[c];  // dequantised K = scale * code value
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = t0 + 16 * c + 4 * qr + i;
-        x[n][c][i] = lim.valid(n, tok, end) ? sacc[i] * sl : -INFINITY;
-        mt[n] = fmaxf(mt[n], x[n][c][i]);
-      }
-    }
+    float sl = scale_log2e;
+    if constexpr (F8) sl *= r.ks[c];  // dequantised K = scale * code value
+    scores_from_kop<TC, NS>(kop, c, t0 + 16 * c, end, qop, sl, qr, x, mt, lim);
   }
-#pragma unroll
-  for (int n = 0; n < NS; ++n) {
-    mt[n] = fmaxf(mt[n], __shfl_xor(mt[n], 16));
-    mt[n] = fmaxf(mt[n], __shfl_xor(mt[n], 32));
-  }
+  column_max<NS>(mt);
 }
 
 // Online-softmax step of one column: the running max takes the tile's max,
@@ -374,6 +392,111 @@ __device__ __forceinline__ float softmax_update(float (&x)[TC][4], float mt, flo
   return alpha;
 }
 
+// Rescales the P.V accumulators by alpha, only when some column's running
+// max moved (alpha == 1 exactly otherwise, so skipping changes no bit); past
+// the first few hundred tokens most tiles skip it.
+template <int NS>
+__device__ __forceinline__ void rescale_lazy(const float (&alpha)[NS], MfmaState<NS>& st) {
+  bool moved = false;
+#pragma unroll
+  for (int n = 0; n < NS; ++n) moved |= alpha[n] != 1.f;
+  if (!PKV_LAZY_RESCALE || __builtin_amdgcn_ballot_w64(moved) != 0) {
+#pragma unroll
+    for (int n = 0; n < NS; ++n)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) st.o[n][j] *= alpha[n];
+  }
+}
+
+// out^T[d][col] += sum_t V[t][d] P[t][col] for chunk c with
+// v_mfma_f32_16x16x16_bf16, 16 dims per product.  B = P: lane (col, qr)
+// already holds P[4 qr + i][col].  p is split into bf16 hi + lo (the top 8
+// and the next 8 mantissa bits), two products each, so p keeps 16 bits.
+// A = V^T from the chunk's 16 V rows in LDS (`vcol`, rows kVRowPad units
+// apart): lane (col, qr) takes V[4 qr + i][16 j + col]; every column set uses
+// the same A operand.
+template <int TC, int NS>
+__device__ __forceinline__ void pv_from_lds(const uint16_t* vcol, int c,
+                                            const float (&x)[NS][TC][4], int col, int qr,
+                                            MfmaState<NS>& st) {
+  bf16x4_t phi[NS], plo[NS];
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    uint32_t hb[4], lb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hb[i] = __float_as_uint(x[n][c][i]) & 0xFFFF0000u;
+      lb[i] = __float_as_uint(x[n][c][i] - __uint_as_float(hb[i]));
+    }
+    const uint32_t hi[2] = {__builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u),
+                            __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u)};
+    const uint32_t lo[2] = {__builtin_amdgcn_perm(lb[1], lb[0], 0x07060302u),
+                            __builtin_amdgcn_perm(lb[3], lb[2], 0x07060302u)};
+    phi[n] = __builtin_bit_cast(bf16x4_t, hi);
+    plo[n] = __builtin_bit_cast(bf16x4_t, lo);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+#if PKV_V_TR_READ
+    const bf16x4_t vt =
+        lds_read_tr16(vcol + (4 * qr + col / 4) * (kVRowPad * 8) + 16 * j + 4 * (col % 4));
+#else
+    uint16_t e[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) e[t] = vcol[(4 * qr + t) * (kVRowPad * 8) + 16 * j + col];
+    const uint32_t va[2] = {e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16)};
+    const bf16x4_t vt = __builtin_bit_cast(bf16x4_t, va);
+#endif
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+      st.o[n][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, phi[n], st.o[n][j], 0, 0, 0);
+      st.o[n][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, plo[n], st.o[n][j], 0, 0, 0);
+    }
+  }
+}
+
+// pv_from_lds for two chunks c0, c1 at once with v_mfma_f32_16x16x32_bf16
+// (twice the rate of the 16-deep product): lane (col, qr)'s eight k-slots are
+// its four tokens of chunk c0 (4 qr + i) followed by its four of chunk c1, in
+// both operands, so the sum over k is unchanged.  The A operand joins two
+// transposing reads, one per chunk (`vcol0`, `vcol1`).
+template <int TC, int NS>
+__device__ __forceinline__ void pv_pair_from_lds(const uint16_t* vcol0, const uint16_t* vcol1,
+                                                 int c0, int c1, const float (&x)[NS][TC][4],
+                                                 int col, int qr, MfmaState<NS>& st) {
+  bf16x8_t phi[NS], plo[NS];
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    uint32_t hb[8], lb[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float v = i < 4 ? x[n][c0][i] : x[n][c1][i - 4];
+      hb[i] = __float_as_uint(v) & 0xFFFF0000u;
+      lb[i] = __float_as_uint(v - __uint_as_float(hb[i]));
+    }
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      hi[k] = __builtin_amdgcn_perm(hb[2 * k + 1], hb[2 * k], 0x07060302u);
+      lo[k] = __builtin_amdgcn_perm(lb[2 * k + 1], lb[2 * k], 0x07060302u);
+    }
+    phi[n] = __builtin_bit_cast(bf16x8_t, hi);
+    plo[n] = __builtin_bit_cast(bf16x8_t, lo);
+  }
+  const int off = (4 * qr + col / 4) * (kVRowPad * 8) + 4 * (col % 4);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const bf16x4_t va = lds_read_tr16(vcol0 + off + 16 * j);
+    const bf16x4_t vb = lds_read_tr16(vcol1 + off + 16 * j);
+    const bf16x8_t vt = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+      st.o[n][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, phi[n], st.o[n][j], 0, 0, 0);
+      st.o[n][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, plo[n], st.o[n][j], 0, 0, 0);
+    }
+  }
+}
+
 // Scores, online-softmax update and P.V accumulation for one loaded tile,
 // P.V on the matrix cores.
 template <int TC, int NS, bool F8, class Lim = WindowTokens>
@@ -394,63 +517,13 @@ __device__ __forceinline__ void compute_tile(const KVTile<TC, F8>& r, int t0, in
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[n][c][i] *= r.vs[c];
   }
-  // out^T[d][col] += sum_t V[t][d] P[t][col] with v_mfma_f32_16x16x16_bf16, 16
-  // dims per tile.  B = P: lane (col, qr) already holds P[4 qr + i][col].  p is
-  // split into bf16 hi + lo (the top 8 and the next 8 mantissa bits), two
-  // products each, so p keeps 16 bits.  A = V^T: lane (col, qr) takes
-  // V[4 qr + i][16 j + col], read column-wise from the V rows this wave wrote
-  // to LDS; every column set uses the same A operand.
-  // Rescale the accumulators only when some column's running max moved
-  // (alpha == 1 exactly otherwise, so skipping changes no bit); past the
-  // first few hundred tokens most tiles skip it.
-  bool moved = false;
-#pragma unroll
-  for (int n = 0; n < NS; ++n) moved |= alpha[n] != 1.f;
-  if (!PKV_LAZY_RESCALE || __builtin_amdgcn_ballot_w64(moved) != 0) {
-#pragma unroll
-    for (int n = 0; n < NS; ++n)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) st.o[n][j] *= alpha[n];
-  }
+  rescale_lazy<NS>(alpha, st);
   const uint16_t* vcol = reinterpret_cast<const uint16_t*>(ctx.v_lds);
 #pragma unroll
   for (int c = 0; c < TC; ++c) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) ctx.v_lds[(4 * qr + i) * kVRowPad + ctx.col] = r.vrow(c, i);
-    bf16x4_t phi[NS], plo[NS];
-#pragma unroll
-    for (int n = 0; n < NS; ++n) {
-      uint32_t hb[4], lb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        hb[i] = __float_as_uint(x[n][c][i]) & 0xFFFF0000u;
-        lb[i] = __float_as_uint(x[n][c][i] - __uint_as_float(hb[i]));
-      }
-      const uint32_t hi[2] = {__builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u),
-                              __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u)};
-      const uint32_t lo[2] = {__builtin_amdgcn_perm(lb[1], lb[0], 0x07060302u),
-                              __builtin_amdgcn_perm(lb[3], lb[2], 0x07060302u)};
-      phi[n] = __builtin_bit_cast(bf16x4_t, hi);
-      plo[n] = __builtin_bit_cast(bf16x4_t, lo);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-#if PKV_V_TR_READ
-      const bf16x4_t vt =
-          lds_read_tr16(vcol + (4 * qr + ctx.col / 4) * (kVRowPad * 8) + 16 * j + 4 * (ctx.col % 4));
-#else
-      uint16_t e[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) e[t] = vcol[(4 * qr + t) * (kVRowPad * 8) + 16 * j + ctx.col];
-      const uint32_t va[2] = {e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16)};
-      const bf16x4_t vt = __builtin_bit_cast(bf16x4_t, va);
-#endif
-#pragma unroll
-      for (int n = 0; n < NS; ++n) {
-        st.o[n][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, phi[n], st.o[n][j], 0, 0, 0);
-        st.o[n][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, plo[n], st.o[n][j], 0, 0, 0);
-      }
-    }
+    pv_from_lds<TC, NS>(vcol, c, x, ctx.col, qr, st);
   }
 }
 
