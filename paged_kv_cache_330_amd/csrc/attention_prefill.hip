@@ -25,7 +25,11 @@
 // waves cuts the K/V reads per query four times against one wave per tile.
 // Items are numbered sequence by sequence from the per-sequence counts (a
 // prefix scan in LDS) and dispatched from the last to the first, so the
-// longest key ranges of each sequence start early.
+// longest key ranges of each sequence start early.  The grid is
+// one-dimensional and XCD-aware: workgroups are dealt round-robin over the
+// eight XCDs, so the linear id is remapped to give each XCD a contiguous
+// range of (kv head, item) pairs: the items of one sequence and kv head then
+// run together on one XCD and re-read their K/V from its L2.
 //
 // Checks: a query range with query_start[b] < 0, query_start[b + 1] <
 // query_start[b], query_start[b + 1] > num_tokens, or more new tokens than
@@ -49,8 +53,18 @@ constexpr int kTC = PKV_PREFILL_CHUNKS;  // chunks per tile
 constexpr int kTileRows = 16 * kTC;      // tokens per tile
 static_assert(kItemThreads == 16 * 16, "one 16-byte unit of 16 rows per lane and chunk");
 
+constexpr int kXcds = 8;  // XCDs of the device; workgroups go round-robin over them
+
+// Bijection of [0, n): workgroup id p (on XCD p % kXcds) -> a logical id such
+// that each XCD holds a contiguous range of logical ids.
+__device__ __forceinline__ int xcd_contiguous(int p, int n) {
+  const int q = n / kXcds, r = n % kXcds;
+  const int xcd = p % kXcds, slot = p / kXcds;
+  return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + slot;
+}
+
 template <int G, int BS>
-__global__ __launch_bounds__(kItemThreads) void prefill_kernel(PrefillArgs pa) {
+__global__ __launch_bounds__(kItemThreads) void prefill_kernel(PrefillArgs pa, int items_ub) {
   static_assert(16 % G == 0, "group must divide 16");
   constexpr int QW = kCols / G;         // new tokens per wave
   constexpr int QT = kItemWaves * QW;   // new tokens per work item
@@ -64,9 +78,11 @@ __global__ __launch_bounds__(kItemThreads) void prefill_kernel(PrefillArgs pa) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int col = lane & 15, qr = lane >> 4;
-  const int kvh = blockIdx.y;
+  const int logical = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int kvh = logical / items_ub;
+  const int item_rev = logical - kvh * items_ub;  // 0: the last item
   const int B = a.num_seqs;
-  const bool reporter = blockIdx.x == 0 && blockIdx.y == 0;
+  const bool reporter = blockIdx.x == 0;
   const int32_t* qs = pa.query_start;
 
   // New tokens of sequence b, or -1 for an inconsistent range.
@@ -83,7 +99,7 @@ __global__ __launch_bounds__(kItemThreads) void prefill_kernel(PrefillArgs pa) {
     const int n = new_tokens(b, reporter);
     return n > 0 ? (n + QT - 1) / QT : 0;
   });
-  const int item = W - 1 - static_cast<int>(blockIdx.x);
+  const int item = W - 1 - item_rev;
   if (item < 0) return;
   const int b = last_at_most(s_item, B, item);
   const int n = new_tokens(b, false);  // > 0: b owns this item
@@ -207,13 +223,16 @@ hipError_t launch_prefill_g(const PrefillArgs& a, int block_size, hipStream_t s)
   constexpr int QT = kItemWaves * kCols / G;
   // Work items: at most ceil(T / QT) + B when the query ranges are consistent.
   const int64_t items = (a.num_tokens + QT - 1) / QT + a.d.num_seqs;
-  const dim3 grid(static_cast<unsigned>(items), a.d.num_kv_heads);
+  const int64_t total = items * a.d.num_kv_heads;
+  if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const int ub = static_cast<int>(items);
+  const dim3 grid(static_cast<unsigned>(total));
   const dim3 block(kItemThreads);
   switch (block_size) {
-    case 8: prefill_kernel<G, 8><<<grid, block, 0, s>>>(a); break;
-    case 16: prefill_kernel<G, 16><<<grid, block, 0, s>>>(a); break;
-    case 32: prefill_kernel<G, 32><<<grid, block, 0, s>>>(a); break;
-    case 64: prefill_kernel<G, 64><<<grid, block, 0, s>>>(a); break;
+    case 8: prefill_kernel<G, 8><<<grid, block, 0, s>>>(a, ub); break;
+    case 16: prefill_kernel<G, 16><<<grid, block, 0, s>>>(a, ub); break;
+    case 32: prefill_kernel<G, 32><<<grid, block, 0, s>>>(a, ub); break;
+    case 64: prefill_kernel<G, 64><<<grid, block, 0, s>>>(a, ub); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -223,7 +242,7 @@ hipError_t launch_prefill_g(const PrefillArgs& a, int block_size, hipStream_t s)
 
 hipError_t launch_prefill(const PrefillArgs& a, int block_size, int group, hipStream_t s) {
   if (a.d.num_seqs < 1 || a.d.num_seqs > kMaxBalancedSeqs || a.num_tokens < 1 ||
-      a.num_tokens > 0x7FFFFFFF || a.d.num_kv_heads > 65535)
+      a.num_tokens > 0x7FFFFFFF)
     return hipErrorInvalidValue;
   switch (group) {
     case 1: return launch_prefill_g<1>(a, block_size, s);
