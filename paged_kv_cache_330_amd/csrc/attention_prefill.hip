@@ -64,7 +64,7 @@ __device__ __forceinline__ int xcd_contiguous(int p, int n) {
 }
 
 template <int G, int BS>
-__global__ __launch_bounds__(kItemThreads) void prefill_kernel(PrefillArgs pa, int items_ub) {
+__global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa, int items_ub) {
   static_assert(16 % G == 0, "group must divide 16");
   constexpr int QW = kCols / G;         // new tokens per wave
   constexpr int QT = kItemWaves * QW;   // new tokens per work item
@@ -72,6 +72,7 @@ __global__ __launch_bounds__(kItemThreads) void prefill_kernel(PrefillArgs pa, i
   __shared__ int s_bt[kMaxPartitionTokens / BS + 1];
   __shared__ u32x4_t s_k[2][kTileRows * kKRowPad];
   __shared__ u32x4_t s_v[2][kTileRows * kVRowPad];
+  __shared__ u32x4_t s_q[kItemWaves][kSharedSets][4][64];  // each lane's Q operands
   __shared__ int s_item[kMaxBalancedSeqs + 1];  // first work item of each sequence
   __shared__ int s_wsum[kItemWaves];
 
@@ -111,14 +112,18 @@ __global__ __launch_bounds__(kItemThreads) void prefill_kernel(PrefillArgs pa, i
   const int wt1 = min(t1, wt0 + QW);
 
   // Columns: query rows and causal limits (a column past the item's last
-  // token repeats it; its output is not stored).
+  // token repeats it; its output is not stored).  The Q operands wait in LDS
+  // (read back for every tile), which leaves the registers to two tiles of
+  // loads in flight.
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
-  bf16x8_t qop[kSharedSets][4];
   CausalTokens<kSharedSets> lim;
 #pragma unroll
   for (int s = 0; s < kSharedSets; ++s) {
     const int t = min(wt0 + (16 * s + col) / G, t1 - 1);
-    load_qop(q + ((int64_t)(r0 + t) * a.num_q_heads + kvh * G + col % G) * kD, qr, qop[s]);
+    bf16x8_t qo[4];
+    load_qop(q + ((int64_t)(r0 + t) * a.num_q_heads + kvh * G + col % G) * kD, qr, qo);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) s_q[wave][s][k][lane] = __builtin_bit_cast(u32x4_t, qo[k]);
     lim.limit[s] = pos0 + t + 1;
   }
   MfmaState<kSharedSets> st;
@@ -140,8 +145,7 @@ __global__ __launch_bounds__(kItemThreads) void prefill_kernel(PrefillArgs pa, i
       s_bt[i] = checked_block(bt, blk0 + i, a.num_blocks, a.err);
     __syncthreads();
     // Rows past the window's end re-read its last token (masked).
-    u32x4_t rk[kTC], rv[kTC];
-    auto load_units = [&](int tt) {
+    auto load_units = [&](int tt, u32x4_t (&rk)[kTC], u32x4_t (&rv)[kTC]) {
 #pragma unroll
       for (int c = 0; c < kTC; ++c) {
         const int tok = min(tt + 16 * c + urow, wend - 1);
@@ -151,21 +155,20 @@ __global__ __launch_bounds__(kItemThreads) void prefill_kernel(PrefillArgs pa, i
         rv[c] = *reinterpret_cast<const u32x4_t*>(vbase + row);
       }
     };
-    auto stage = [&](int buf) {
+    auto stage = [&](int buf, const u32x4_t (&rk)[kTC], const u32x4_t (&rv)[kTC]) {
 #pragma unroll
       for (int c = 0; c < kTC; ++c) {
         s_k[buf][(16 * c + urow) * kKRowPad + ucol] = rk[c];
         s_v[buf][(16 * c + urow) * kVRowPad + ucol] = rv[c];
       }
     };
-    load_units(w0);
-    stage(0);
-    const int ntile = (wend - w0 + kTileRows - 1) / kTileRows;
-    for (int i = 0; i < ntile; ++i) {
-      const int tt = w0 + kTileRows * i;
-      load_units(tt + kTileRows);  // next tile (past the end: re-reads, unused)
-      __syncthreads();             // tile i is in buffer i & 1; tile i - 1 is done
-      const u32x4_t* kt = s_k[i & 1];
+    auto compute = [&](int buf, int tt) {
+      bf16x8_t qop[kSharedSets][4];
+#pragma unroll
+      for (int m = 0; m < kSharedSets; ++m)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) qop[m][k] = __builtin_bit_cast(bf16x8_t, s_q[wave][m][k][lane]);
+      const u32x4_t* kt = s_k[buf];
       float x[kSharedSets][kTC][4], mt[kSharedSets], alpha[kSharedSets];
 #pragma unroll
       for (int m = 0; m < kSharedSets; ++m) mt[m] = -INFINITY;
@@ -182,7 +185,7 @@ __global__ __launch_bounds__(kItemThreads) void prefill_kernel(PrefillArgs pa, i
       for (int m = 0; m < kSharedSets; ++m)
         alpha[m] = softmax_update<kTC>(x[m], mt[m], st.m[m], st.l[m]);
       rescale_lazy<kSharedSets>(alpha, st);
-      const uint16_t* vt = reinterpret_cast<const uint16_t*>(s_v[i & 1]);
+      const uint16_t* vt = reinterpret_cast<const uint16_t*>(s_v[buf]);
 #if PKV_PREFILL_PV32
 #pragma unroll
       for (int c = 0; c + 1 < kTC; c += 2)
@@ -197,7 +200,32 @@ __global__ __launch_bounds__(kItemThreads) void prefill_kernel(PrefillArgs pa, i
       for (int c = 0; c < kTC; ++c)
         pv_from_lds<kTC, kSharedSets>(vt + 16 * c * kVRowPad * 8, c, x, col, qr, st);
 #endif
-      stage((i + 1) & 1);  // tile i + 1
+    };
+    // Two tiles in flight: registers a and b alternate, tile t is computed
+    // from LDS buffer t & 1 while tiles t + 1 (staged next) and t + 2 load.
+    // Pairs of tiles with a single loop exit (an exit per half makes the
+    // compiler wait for every load at the loop head).
+    constexpr int T = kTileRows;
+    const int ntile = (wend - w0 + T - 1) / T;
+    u32x4_t ka[kTC], va[kTC], kb[kTC], vb[kTC];
+    load_units(w0, ka, va);
+    load_units(w0 + T, kb, vb);
+    stage(0, ka, va);
+    const int npair = ntile >> 1;
+    for (int p = 0; p < npair; ++p) {
+      const int tt = w0 + 2 * T * p;
+      load_units(tt + 2 * T, ka, va);  // tile 2p + 2
+      __syncthreads();                 // tile 2p is in buffer 0; tile 2p - 1 is done
+      compute(0, tt);
+      stage(1, kb, vb);                // tile 2p + 1
+      load_units(tt + 3 * T, kb, vb);  // tile 2p + 3
+      __syncthreads();
+      compute(1, tt + T);
+      stage(0, ka, va);                // tile 2p + 2
+    }
+    if (ntile & 1) {
+      __syncthreads();
+      compute(0, w0 + 2 * T * npair);
     }
   }
 
