@@ -25,7 +25,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mfma_kernel(DecodeArgs 
   static_assert(16 % G == 0, "group must divide 16");
   __shared__ int s_bt[kMaxPartitionTokens / BS + 1];
   __shared__ u32x4_t s_kt[PKV_K_VIA_LDS ? kMaxWaves * 16 * kKRowPad : 1];
-  __shared__ u32x4_t s_vt[kPvOnMfma<G> ? kMaxWaves * 16 * kVRowPad : 1];
+  __shared__ u32x4_t s_vt[kPvOnMfma<G> ? kMaxWaves * 16 * TC * kVRowPad : 1];
   const int kh = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kvh = blockIdx.x * kh + wave;
@@ -42,7 +42,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mfma_kernel(DecodeArgs 
   WaveState<G> st;
   st.reset();
   attend_range<G, BS, TC, F8>(a, s_bt, s_kt + (PKV_K_VIA_LDS ? wave * 16 * kKRowPad : 0),
-                          s_vt + (kPvOnMfma<G> ? wave * 16 * kVRowPad : 0), b, kvh, pt.begin,
+                          s_vt + (kPvOnMfma<G> ? wave * 16 * TC * kVRowPad : 0), b, kvh, pt.begin,
                           pt.end, qop, st);
   Sink sink{nullptr, nullptr, nullptr, 0, 0};
   if (pt.count > 1) {
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) PKV_BALANCED_OCCUPANCY void decode_
   static_assert(16 % G == 0, "group must divide 16");
   __shared__ int s_bt[kMaxPartitionTokens / BS + 1];
   __shared__ u32x4_t s_kt[PKV_K_VIA_LDS ? kMaxWaves * 16 * kKRowPad : 1];
-  __shared__ u32x4_t s_vt[kPvOnMfma<G> ? kMaxWaves * 16 * kVRowPad : 1];
+  __shared__ u32x4_t s_vt[kPvOnMfma<G> ? kMaxWaves * 16 * TC * kVRowPad : 1];
   __shared__ int s_cc[kMaxBalancedSeqs + 1];
   __shared__ int s_wsum[kMaxWaves];
 
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) PKV_BALANCED_OCCUPANCY void decode_
     WaveState<G> st;
     st.reset();
     attend_range<G, BS, TC, F8>(a, s_bt, s_kt + (PKV_K_VIA_LDS ? wave * 16 * kKRowPad : 0),
-                            s_vt + (kPvOnMfma<G> ? wave * 16 * kVRowPad : 0), b, kvh, tok_begin,
+                            s_vt + (kPvOnMfma<G> ? wave * 16 * TC * kVRowPad : 0), b, kvh, tok_begin,
                             tok_end, qop, st);
     Sink sink{nullptr, nullptr, nullptr, 0, 0};
     if (!(first && last))

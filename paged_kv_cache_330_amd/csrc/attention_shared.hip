@@ -83,6 +83,7 @@ __device__ __forceinline__ void store_columns(const DecodeArgs& a, MfmaState<NS>
 template <int G, int BS, int TC>
 __global__ __launch_bounds__(kMaxWaves * 64) void decode_shared_kernel(SharedArgs sa) {
   static_assert(16 % G == 0, "group must divide 16");
+  static_assert(TC == 1, "V tiles hold one 16-row chunk per wave (LDS is nearly full)");
   constexpr int MPS = kMembers<G>;
   const DecodeArgs& a = sa.d;
   __shared__ int s_bt[kMaxPartitionTokens / BS + 1];
@@ -314,7 +315,7 @@ __global__ __launch_bounds__(256) void shared_merge_kernel(SharedArgs sa) {
 
 template <int G>
 hipError_t launch_shared_g(const SharedArgs& a, int block_size, int kh, hipStream_t s) {
-  constexpr int TC = PKV_MFMA_TILE_CHUNKS;
+  constexpr int TC = 1;  // one chunk per tile: the V tiles are sized for 16 rows
   const dim3 grid(a.d.num_kv_heads / kh, a.d.slices);
   const dim3 block(kh * 64);
   switch (block_size) {

@@ -519,11 +519,25 @@ __device__ __forceinline__ void compute_tile(const KVTile<TC, F8>& r, int t0, in
   }
   rescale_lazy<NS>(alpha, st);
   const uint16_t* vcol = reinterpret_cast<const uint16_t*>(ctx.v_lds);
+  if constexpr (TC % 2 == 0 && PKV_PV_PAIRS) {
+    // all chunks' V rows to LDS (chunk c at rows 16 c ..), then P.V of
+    // chunk pairs with the 16x16x32 product
 #pragma unroll
-  for (int c = 0; c < TC; ++c) {
+    for (int c = 0; c < TC; ++c)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ctx.v_lds[(4 * qr + i) * kVRowPad + ctx.col] = r.vrow(c, i);
-    pv_from_lds<TC, NS>(vcol, c, x, ctx.col, qr, st);
+      for (int i = 0; i < 4; ++i)
+        ctx.v_lds[(16 * c + 4 * qr + i) * kVRowPad + ctx.col] = r.vrow(c, i);
+#pragma unroll
+    for (int c = 0; c < TC; c += 2)
+      pv_pair_from_lds<TC, NS>(vcol + 16 * c * kVRowPad * 8, vcol + 16 * (c + 1) * kVRowPad * 8,
+                               c, c + 1, x, ctx.col, qr, st);
+  } else {
+#pragma unroll
+    for (int c = 0; c < TC; ++c) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ctx.v_lds[(4 * qr + i) * kVRowPad + ctx.col] = r.vrow(c, i);
+      pv_from_lds<TC, NS>(vcol, c, x, ctx.col, qr, st);
+    }
   }
 }
 

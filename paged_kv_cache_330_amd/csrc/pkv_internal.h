@@ -39,6 +39,9 @@ constexpr int kMaxBalancedSeqs = 2048;     // batch limit of the balanced schedu
 #ifndef PKV_DRAIN_PREFETCH
 #define PKV_DRAIN_PREFETCH 1    // drain the prefetch past a window's end before leaving it
 #endif
+#ifndef PKV_PV_PAIRS
+#define PKV_PV_PAIRS 1          // several chunks per tile: P.V of chunk pairs with the 16x16x32 product
+#endif
 #ifndef PKV_LAZY_RESCALE
 #define PKV_LAZY_RESCALE 1      // P.V accumulators rescaled only in tiles where a running max moved
 #endif
