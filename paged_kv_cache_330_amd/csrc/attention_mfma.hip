@@ -257,8 +257,8 @@ namespace {
 
 template <bool F8>
 hipError_t launch_mfma_typed(const DecodeArgs& a, int block_size, int group, hipStream_t s) {
-  const int kh = mfma_waves_per_group(a.num_kv_heads);
   if (a.slices > 0) {
+    const int kh = balanced_waves_per_group(a.num_kv_heads);
     if (a.num_seqs > kMaxBalancedSeqs) return hipErrorInvalidValue;
     switch (group) {
       case 1: return launch_balanced_g<1, F8>(a, block_size, kh, s);
@@ -268,6 +268,7 @@ hipError_t launch_mfma_typed(const DecodeArgs& a, int block_size, int group, hip
       default: return hipErrorInvalidValue;
     }
   }
+  const int kh = mfma_waves_per_group(a.num_kv_heads);
   switch (group) {
     case 1: return launch_partitions_g<1, F8>(a, block_size, kh, s);
     case 2: return launch_partitions_g<2, F8>(a, block_size, kh, s);

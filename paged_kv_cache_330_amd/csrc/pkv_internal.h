@@ -57,6 +57,9 @@ constexpr int kMaxBalancedSeqs = 2048;     // batch limit of the balanced schedu
 #ifndef PKV_BALANCED_WAVES_PER_EU
 #define PKV_BALANCED_WAVES_PER_EU 0  // > 0: ask the compiler for this occupancy (may spill)
 #endif
+#ifndef PKV_BALANCED_MAX_WAVES
+#define PKV_BALANCED_MAX_WAVES 8 // most waves (kv heads) per workgroup of the balanced schedule
+#endif
 #ifndef PKV_BALANCED_WGS
 #define PKV_BALANCED_WGS 256    // workgroups of the balanced schedule (all kv-head groups)
 #endif
@@ -69,8 +72,14 @@ constexpr int kMaxBalancedSeqs = 2048;     // batch limit of the balanced schedu
 int mfma_waves_per_group(int num_kv_heads);
 
 // Slices of the balanced schedule (per kv-head group).
+// Waves (kv heads) per workgroup of the balanced schedule.
+inline int balanced_waves_per_group(int num_kv_heads) {
+  const int kh = mfma_waves_per_group(num_kv_heads);
+  return kh < PKV_BALANCED_MAX_WAVES ? kh : PKV_BALANCED_MAX_WAVES;
+}
+
 inline int balanced_slices(int num_kv_heads) {
-  const int groups = num_kv_heads / mfma_waves_per_group(num_kv_heads);
+  const int groups = num_kv_heads / balanced_waves_per_group(num_kv_heads);
   return (PKV_BALANCED_WGS + groups - 1) / groups;
 }
 

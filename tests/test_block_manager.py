@@ -258,3 +258,31 @@ def test_shared_prefix_groups_random_forks():
             firsts.setdefault(m.block_table(s)[0], []).append(s)
         for blk, seqs in firsts.items():
             assert (len(seqs) >= 2) == all(s in seen for s in seqs)
+
+
+def test_fp8_block_scales_recipe():
+    # Input preparation for FP8 pools: per (block, kv head), the largest
+    # magnitude among the tokens written to the block, over 448; 1.0 when
+    # that is 0; the `unused` value for blocks that get no token.  Worked by
+    # hand on 3 tokens in 2 blocks of 2 slots, 2 kv heads of 2 dims.
+    import numpy as np
+    from paged_kv_cache_330_amd.workloads import bf16_round, fp8_block_scales
+    k = bf16_round(np.array([[[1.0, -3.0], [0.0, 0.0]],
+                             [[2.0, 0.5], [0.0, 0.0]],
+                             [[-8.0, 4.0], [448.0, 1.0]]], np.float32))
+    v = bf16_round(np.array([[[0.25, 0.0], [1.0, 1.0]],
+                             [[0.0, 0.0], [0.0, -2.0]],
+                             [[1.0, 1.0], [1.0, 1.0]]], np.float32))
+    slots = np.array([0, 1, 4])  # block 0 (two tokens), block 2 (one token); block 1 unused
+    ks, vs = fp8_block_scales(k, v, slots, num_blocks=3, block_size=2)
+    assert ks.dtype == np.float32 and ks.shape == (3, 2)
+    assert ks[0, 0] == np.float32(3.0) / np.float32(448) and ks[0, 1] == np.float32(1.0)
+    assert ks[2, 0] == np.float32(8.0) / np.float32(448) and ks[2, 1] == np.float32(1.0)
+    assert vs[0, 0] == np.float32(0.25) / np.float32(448) and vs[0, 1] == np.float32(2.0) / np.float32(448)
+    assert np.isnan(ks[1]).all() and np.isnan(vs[1]).all()
+    ks1, _ = fp8_block_scales(k, v, slots, num_blocks=3, block_size=2, unused=1.0)
+    assert (ks1[1] == 1.0).all()
+    # skipped slots (-1) contribute nothing
+    ks2, vs2 = fp8_block_scales(k, v, np.array([0, -1, 4]), num_blocks=3, block_size=2)
+    assert ks2[0, 0] == np.float32(3.0) / np.float32(448)
+    assert vs2[0, 1] == np.float32(1.0) / np.float32(448)  # token 1's -2 is not written
