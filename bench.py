@@ -606,9 +606,10 @@ PREFILL_WORKLOADS = [
 def prefill_report(torch, ops, reps=10):
     """Paged prefill of Llama-3-8B-shaped prompts (32 q / 8 kv heads, head_dim
     128, bf16, block size 16): the write of every prompt token through the
-    slot mapping, then causal attention of the new tokens.  The attention is
-    bound by the matrix cores: algorithmic flops = 4 D Hq (p + 1) per new
-    token at position p, against the dense bf16 MFMA peak."""
+    slot mapping, then causal attention of the new tokens; then the same over
+    FP8 E4M3 pools.  The attention is bound by the matrix cores: algorithmic
+    flops = 4 D Hq (p + 1) per new token at position p, against the dense
+    bf16 MFMA peak."""
     from paged_kv_cache_330_amd.workloads import (PrefillWorkload, empty_device_caches,
                                                   torch_tensor)
     dev = "cuda"
@@ -650,8 +651,31 @@ def prefill_report(torch, ops, reps=10):
         res["attn_tflops"] = round(tflops, 1)
         res["attn_mfma_frac"] = round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)
         res["prompt_tokens_per_s"] = round(w.num_tokens / ((res["t_write_us"] + res["t_attn_us"]) * 1e-6), 1)
+        # the same prompts over FP8 E4M3 pools (max-abs block scales)
+        from paged_kv_cache_330_amd.workloads import fp8_block_scales
+        ks_h, vs_h = fp8_block_scales(w.k_tokens, w.v_tokens, w.slots, w.num_blocks, 16, unused=1.0)
+        ks, vs = torch.from_numpy(ks_h).to(dev), torch.from_numpy(vs_h).to(dev)
+        k8 = torch.zeros(kc.shape, dtype=torch.uint8, device=dev)
+        v8 = torch.zeros_like(k8)
+        write8 = lambda: ops.pkv_kv_write_fp8(kt, vt, slots, k8, v8, ks, vs)  # noqa: E731
+        attend8 = lambda: ops.pkv_attention_prefill_fp8(out, q, qs, k8, v8, ks, vs, bt, sl,  # noqa: E731
+                                                        float(w.scale))
+        for label, call in (("write_fp8", write8), ("attn_fp8", attend8)):
+            call()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                call()
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            ops.pkv_check_device_errors()
+            res[f"t_{label}_us"] = round(statistics.median(ts) * 1e3, 2)
+        res["attn_fp8_tflops"] = round(flops / (res["t_attn_fp8_us"] * 1e-6) / 1e12, 1)
         print(json.dumps({"report": res}), flush=True)
-        del kc, vc, kt, vt
+        del kc, vc, kt, vt, k8, v8
         torch.cuda.empty_cache()
 
 

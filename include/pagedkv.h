@@ -304,6 +304,20 @@ int pkv_attention_decode_fp8(void* out, int32_t out_dtype, const void* q,
                              size_t workspace_bytes, void* stream);
 
 /*
+ * Prefill attention over FP8 pools: the result pkv_attention_prefill gives
+ * for pools holding the dequantized values scale * value(code) (q is bf16).
+ * All other arguments mean what they mean for pkv_attention_prefill; the
+ * prompt's K/V are written first with pkv_kv_write_fp8.  Scales are used as
+ * given.
+ */
+int pkv_attention_prefill_fp8(void* out, int32_t out_dtype, const void* q, int64_t num_tokens,
+                              const int32_t* query_start, const void* k_cache,
+                              const void* v_cache, const float* k_scale, const float* v_scale,
+                              const pkv_cache_desc* cache, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                              int32_t num_seqs, int32_t num_q_heads, float scale, void* stream);
+
+/*
  * pkv_block_copy for FP8 pools: each pair copies the K and V codes of the
  * block and its num_kv_heads K and V scales, so that a copied block decodes
  * to the same values.

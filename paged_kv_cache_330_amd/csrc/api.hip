@@ -454,17 +454,28 @@ int pkv_attention_decode_shared(void* out, int32_t out_dtype, const void* q, con
   return e == hipSuccess ? PKV_OK : hip_fail(e, "attention_decode_shared launch");
 }
 
-int pkv_attention_prefill(void* out, int32_t out_dtype, const void* q, int64_t num_tokens,
-                          const int32_t* query_start, const void* k_cache, const void* v_cache,
-                          const pkv_cache_desc* cache, const int32_t* block_tables,
-                          int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
-                          int32_t num_q_heads, float scale, void* stream) {
-  g_last_error.clear();
+}  // extern "C"
+
+namespace {
+
+// Both prefill calls: FP8 pools bring their scales.
+int prefill_common(void* out, int32_t out_dtype, const void* q, int64_t num_tokens,
+                   const int32_t* query_start, const void* k_cache, const void* v_cache,
+                   const float* k_scale, const float* v_scale, const pkv_cache_desc* cache,
+                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                   const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
+                   void* stream, bool fp8) {
   Plan base;
   PKV_TRY(make_plan(cache, num_seqs, num_q_heads, max_blocks_per_seq, 0, &base));
   PKV_TRY(check_decode_scalars(cache, num_q_heads, out_dtype, scale));
-  if (cache->dtype != PKV_BF16 || cache->head_dim != 128)
-    return fail(PKV_ERR_UNSUPPORTED, "prefill attention needs bf16 pools with head_dim 128");
+  if (fp8) {
+    PKV_TRY(check_fp8(cache, "pkv_attention_prefill_fp8"));
+  } else {
+    PKV_TRY(check_not_fp8(cache, "pkv_attention_prefill"));
+  }
+  if (cache->head_dim != 128 || (!fp8 && cache->dtype != PKV_BF16))
+    return fail(PKV_ERR_UNSUPPORTED, "prefill attention needs %s pools with head_dim 128",
+                fp8 ? "FP8" : "bf16");
   if (num_seqs > pkv::kMaxBalancedSeqs)
     return fail(PKV_ERR_UNSUPPORTED, "prefill attention takes at most %d sequences, got %d",
                 pkv::kMaxBalancedSeqs, num_seqs);
@@ -475,12 +486,45 @@ int pkv_attention_prefill(void* out, int32_t out_dtype, const void* q, int64_t n
   PKV_TRY(fill_decode_args(out, out_dtype, q, k_cache, v_cache, cache, block_tables,
                            max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, scale, &pa.d));
   PKV_TRY(check_ptr(query_start, 4, "query_start"));
+  if (fp8) {
+    PKV_TRY(check_ptr(k_scale, 4, "k_scale"));
+    PKV_TRY(check_ptr(v_scale, 4, "v_scale"));
+    pa.d.k_scale = k_scale;
+    pa.d.v_scale = v_scale;
+  }
   PKV_TRY(error_word(&pa.d.err));
   pa.query_start = query_start;
   pa.num_tokens = num_tokens;
   hipError_t e = pkv::launch_prefill(pa, cache->block_size, num_q_heads / cache->num_kv_heads,
-                                     static_cast<hipStream_t>(stream));
+                                     static_cast<hipStream_t>(stream), fp8);
   return e == hipSuccess ? PKV_OK : hip_fail(e, "attention_prefill launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_attention_prefill(void* out, int32_t out_dtype, const void* q, int64_t num_tokens,
+                          const int32_t* query_start, const void* k_cache, const void* v_cache,
+                          const pkv_cache_desc* cache, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                          int32_t num_q_heads, float scale, void* stream) {
+  g_last_error.clear();
+  return prefill_common(out, out_dtype, q, num_tokens, query_start, k_cache, v_cache, nullptr,
+                        nullptr, cache, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
+                        num_q_heads, scale, stream, false);
+}
+
+int pkv_attention_prefill_fp8(void* out, int32_t out_dtype, const void* q, int64_t num_tokens,
+                              const int32_t* query_start, const void* k_cache,
+                              const void* v_cache, const float* k_scale, const float* v_scale,
+                              const pkv_cache_desc* cache, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                              int32_t num_seqs, int32_t num_q_heads, float scale, void* stream) {
+  g_last_error.clear();
+  return prefill_common(out, out_dtype, q, num_tokens, query_start, k_cache, v_cache, k_scale,
+                        v_scale, cache, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
+                        num_q_heads, scale, stream, true);
 }
 
 int pkv_kv_write_fp8(const void* k, const void* v, const int64_t* slot_mapping,

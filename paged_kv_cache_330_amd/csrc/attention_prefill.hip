@@ -1,7 +1,8 @@
 // Prefill attention over the paged pools: a chunk of new tokens per sequence
 // (a whole prompt, or the next part of one after cached context) attends
-// causally to the sequence's cached tokens.  bf16 pools with head_dim 128, on
-// the matrix cores of gfx950.
+// causally to the sequence's cached tokens.  bf16 or FP8 E4M3 pools (with a
+// scale per block and kv head) with head_dim 128, on the matrix cores of
+// gfx950.
 //
 // What is computed ("Paged KV" wiki, section "运行阶段": at prefill a sequence
 // takes blocks in order and its K/V are filled in; section "Attention Kernel
@@ -63,7 +64,23 @@ __device__ __forceinline__ int xcd_contiguous(int p, int n) {
   return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + slot;
 }
 
-template <int G, int BS>
+// One lane's share of a 32-token K/V tile in registers, between its loads
+// and its staging into LDS: per 16-token chunk, one 16-byte unit of bf16
+// (8 dims) of a K row and of a V row, or for FP8 pools the 8 codes of those
+// dims and the scales of the row's block.
+template <bool F8>
+struct TileUnits;
+template <>
+struct TileUnits<false> {
+  u32x4_t k[kTC], v[kTC];
+};
+template <>
+struct TileUnits<true> {
+  u32x2_t k[kTC], v[kTC];
+  float ks[kTC], vs[kTC];
+};
+
+template <int G, int BS, bool F8>
 __global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa, int items_ub) {
   static_assert(16 % G == 0, "group must divide 16");
   constexpr int QW = kCols / G;         // new tokens per wave
@@ -72,6 +89,8 @@ __global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa
   __shared__ int s_bt[kMaxPartitionTokens / BS + 1];
   __shared__ u32x4_t s_k[2][kTileRows * kKRowPad];
   __shared__ u32x4_t s_v[2][kTileRows * kVRowPad];
+  __shared__ float s_ks[2][F8 ? kTileRows : 1];  // FP8 pools: K and V scale of each row's block
+  __shared__ float s_vs[2][F8 ? kTileRows : 1];
   __shared__ u32x4_t s_q[kItemWaves][kSharedSets][4][64];  // each lane's Q operands
   __shared__ int s_item[kMaxBalancedSeqs + 1];  // first work item of each sequence
   __shared__ int s_wsum[kItemWaves];
@@ -134,6 +153,8 @@ __global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa
   const int64_t tok_stride = (int64_t)a.num_kv_heads * kD;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k_cache) + (int64_t)kvh * kD + 8 * ucol;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v_cache) + (int64_t)kvh * kD + 8 * ucol;
+  const uint8_t* kbase8 = static_cast<const uint8_t*>(a.k_cache) + (int64_t)kvh * kD + 8 * ucol;
+  const uint8_t* vbase8 = static_cast<const uint8_t*>(a.v_cache) + (int64_t)kvh * kD + 8 * ucol;
   const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
   const int kend = pos0 + t1;  // key tokens of the item: 0 .. kend - 1
   for (int w0 = 0; w0 < kend; w0 += kMaxPartitionTokens) {
@@ -145,21 +166,39 @@ __global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa
       s_bt[i] = checked_block(bt, blk0 + i, a.num_blocks, a.err);
     __syncthreads();
     // Rows past the window's end re-read its last token (masked).
-    auto load_units = [&](int tt, u32x4_t (&rk)[kTC], u32x4_t (&rv)[kTC]) {
+    auto load_units = [&](int tt, TileUnits<F8>& u) {
 #pragma unroll
       for (int c = 0; c < kTC; ++c) {
         const int tok = min(tt + 16 * c + urow, wend - 1);
-        const int64_t row =
-            ((int64_t)s_bt[tok / BS - blk0] * BS + (tok & (BS - 1))) * tok_stride;
-        rk[c] = *reinterpret_cast<const u32x4_t*>(kbase + row);
-        rv[c] = *reinterpret_cast<const u32x4_t*>(vbase + row);
+        const int phys = s_bt[tok / BS - blk0];
+        const int64_t row = ((int64_t)phys * BS + (tok & (BS - 1))) * tok_stride;
+        if constexpr (F8) {
+          u.k[c] = *reinterpret_cast<const u32x2_t*>(kbase8 + row);
+          u.v[c] = *reinterpret_cast<const u32x2_t*>(vbase8 + row);
+          u.ks[c] = a.k_scale[(int64_t)phys * a.num_kv_heads + kvh];
+          u.vs[c] = a.v_scale[(int64_t)phys * a.num_kv_heads + kvh];
+        } else {
+          u.k[c] = *reinterpret_cast<const u32x4_t*>(kbase + row);
+          u.v[c] = *reinterpret_cast<const u32x4_t*>(vbase + row);
+        }
       }
     };
-    auto stage = [&](int buf, const u32x4_t (&rk)[kTC], const u32x4_t (&rv)[kTC]) {
+    // FP8 codes are widened to bf16 here (exactly), so the tile in LDS has
+    // the layout of bf16 pools; the scales go beside it, one per row.
+    auto stage = [&](int buf, const TileUnits<F8>& u) {
 #pragma unroll
       for (int c = 0; c < kTC; ++c) {
-        s_k[buf][(16 * c + urow) * kKRowPad + ucol] = rk[c];
-        s_v[buf][(16 * c + urow) * kVRowPad + ucol] = rv[c];
+        if constexpr (F8) {
+          s_k[buf][(16 * c + urow) * kKRowPad + ucol] = widen_e4m3(u.k[c]);
+          s_v[buf][(16 * c + urow) * kVRowPad + ucol] = widen_e4m3(u.v[c]);
+          if (ucol == 0) {
+            s_ks[buf][16 * c + urow] = u.ks[c];
+            s_vs[buf][16 * c + urow] = u.vs[c];
+          }
+        } else {
+          s_k[buf][(16 * c + urow) * kKRowPad + ucol] = u.k[c];
+          s_v[buf][(16 * c + urow) * kVRowPad + ucol] = u.v[c];
+        }
       }
     };
     auto compute = [&](int buf, int tt) {
@@ -177,13 +216,25 @@ __global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa
         u32x4_t kop[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) kop[s] = kt[(16 * c + col) * kKRowPad + 4 * s + qr];
-        scores_from_kop<kTC, kSharedSets>(kop, c, tt + 16 * c, wend, qop, a.scale_log2e, qr, x,
-                                          mt, lim);
+        // FP8: the lane's 4 rows (4 qr ..) lie in one block; its K scale
+        // multiplies their scores
+        const float sl = F8 ? a.scale_log2e * s_ks[buf][16 * c + 4 * qr] : a.scale_log2e;
+        scores_from_kop<kTC, kSharedSets>(kop, c, tt + 16 * c, wend, qop, sl, qr, x, mt, lim);
       }
       column_max<kSharedSets>(mt);
 #pragma unroll
       for (int m = 0; m < kSharedSets; ++m)
         alpha[m] = softmax_update<kTC>(x[m], mt[m], st.m[m], st.l[m]);
+      if constexpr (F8) {  // dequantised V = scale * code: scale the probabilities (not l)
+#pragma unroll
+        for (int c = 0; c < kTC; ++c) {
+          const float vsc = s_vs[buf][16 * c + 4 * qr];
+#pragma unroll
+          for (int m = 0; m < kSharedSets; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[m][c][i] *= vsc;
+        }
+      }
       rescale_lazy<kSharedSets>(alpha, st);
       const uint16_t* vt = reinterpret_cast<const uint16_t*>(s_v[buf]);
 #if PKV_PREFILL_PV32
@@ -207,21 +258,21 @@ __global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa
     // compiler wait for every load at the loop head).
     constexpr int T = kTileRows;
     const int ntile = (wend - w0 + T - 1) / T;
-    u32x4_t ka[kTC], va[kTC], kb[kTC], vb[kTC];
-    load_units(w0, ka, va);
-    load_units(w0 + T, kb, vb);
-    stage(0, ka, va);
+    TileUnits<F8> ua, ub;
+    load_units(w0, ua);
+    load_units(w0 + T, ub);
+    stage(0, ua);
     const int npair = ntile >> 1;
     for (int p = 0; p < npair; ++p) {
       const int tt = w0 + 2 * T * p;
-      load_units(tt + 2 * T, ka, va);  // tile 2p + 2
+      load_units(tt + 2 * T, ua);  // tile 2p + 2
       __syncthreads();                 // tile 2p is in buffer 0; tile 2p - 1 is done
       compute(0, tt);
-      stage(1, kb, vb);                // tile 2p + 1
-      load_units(tt + 3 * T, kb, vb);  // tile 2p + 3
+      stage(1, ub);                // tile 2p + 1
+      load_units(tt + 3 * T, ub);  // tile 2p + 3
       __syncthreads();
       compute(1, tt + T);
-      stage(0, ka, va);                // tile 2p + 2
+      stage(0, ua);                // tile 2p + 2
     }
     if (ntile & 1) {
       __syncthreads();
@@ -246,7 +297,7 @@ __global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa
   }
 }
 
-template <int G>
+template <int G, bool F8>
 hipError_t launch_prefill_g(const PrefillArgs& a, int block_size, hipStream_t s) {
   constexpr int QT = kItemWaves * kCols / G;
   // Work items: at most ceil(T / QT) + B when the query ranges are consistent.
@@ -257,28 +308,35 @@ hipError_t launch_prefill_g(const PrefillArgs& a, int block_size, hipStream_t s)
   const dim3 grid(static_cast<unsigned>(total));
   const dim3 block(kItemThreads);
   switch (block_size) {
-    case 8: prefill_kernel<G, 8><<<grid, block, 0, s>>>(a, ub); break;
-    case 16: prefill_kernel<G, 16><<<grid, block, 0, s>>>(a, ub); break;
-    case 32: prefill_kernel<G, 32><<<grid, block, 0, s>>>(a, ub); break;
-    case 64: prefill_kernel<G, 64><<<grid, block, 0, s>>>(a, ub); break;
+    case 8: prefill_kernel<G, 8, F8><<<grid, block, 0, s>>>(a, ub); break;
+    case 16: prefill_kernel<G, 16, F8><<<grid, block, 0, s>>>(a, ub); break;
+    case 32: prefill_kernel<G, 32, F8><<<grid, block, 0, s>>>(a, ub); break;
+    case 64: prefill_kernel<G, 64, F8><<<grid, block, 0, s>>>(a, ub); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+template <bool F8>
+hipError_t launch_prefill_typed(const PrefillArgs& a, int block_size, int group, hipStream_t s) {
+  switch (group) {
+    case 1: return launch_prefill_g<1, F8>(a, block_size, s);
+    case 2: return launch_prefill_g<2, F8>(a, block_size, s);
+    case 4: return launch_prefill_g<4, F8>(a, block_size, s);
+    case 8: return launch_prefill_g<8, F8>(a, block_size, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs& a, int block_size, int group, hipStream_t s) {
+hipError_t launch_prefill(const PrefillArgs& a, int block_size, int group, hipStream_t s,
+                          bool fp8) {
   if (a.d.num_seqs < 1 || a.d.num_seqs > kMaxBalancedSeqs || a.num_tokens < 1 ||
       a.num_tokens > 0x7FFFFFFF)
     return hipErrorInvalidValue;
-  switch (group) {
-    case 1: return launch_prefill_g<1>(a, block_size, s);
-    case 2: return launch_prefill_g<2>(a, block_size, s);
-    case 4: return launch_prefill_g<4>(a, block_size, s);
-    case 8: return launch_prefill_g<8>(a, block_size, s);
-    default: return hipErrorInvalidValue;
-  }
+  return fp8 ? launch_prefill_typed<true>(a, block_size, group, s)
+             : launch_prefill_typed<false>(a, block_size, group, s);
 }
 
 }  // namespace pkv

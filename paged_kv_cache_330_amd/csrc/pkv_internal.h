@@ -202,6 +202,7 @@ struct PrefillArgs {
   int64_t num_tokens;           // rows of q and out
 };
 
-hipError_t launch_prefill(const PrefillArgs& a, int block_size, int group, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, int block_size, int group, hipStream_t s,
+                          bool fp8 = false);
 
 }  // namespace pkv

@@ -29,6 +29,7 @@ __all__ = [
     "pkv_attention_prefill",
     "pkv_kv_write_fp8",
     "pkv_attention_decode_fp8",
+    "pkv_attention_prefill_fp8",
     "pkv_block_copy_fp8",
     "pkv_block_transfer_fp8",
     "pkv_check_device_errors",
@@ -95,13 +96,16 @@ def load_library() -> ctypes.CDLL:
     lib.pkv_kv_write_fp8.argtypes = [P, P, P, I64, P, P, P, P, D, P]
     lib.pkv_attention_decode_fp8.argtypes = [P, I32, P, P, P, P, P, D, P, I32, P, I32, I32,
                                              ctypes.c_float, I32, P, SZ, P]
+    lib.pkv_attention_prefill_fp8.argtypes = [P, I32, P, I64, P, P, P, P, P, D, P, I32, P, I32,
+                                              I32, ctypes.c_float, P]
     lib.pkv_block_copy_fp8.argtypes = [P, P, P, P, D, P, I64, P]
     lib.pkv_block_transfer_fp8.argtypes = [P, P, P, P, D, P, P, P, P, D, P, I64, P]
     lib.pkv_last_error.restype = ctypes.c_char_p
     lib.pkv_check_device_errors.argtypes = [P]
     for name in ("pkv_kv_write", "pkv_block_copy", "pkv_block_transfer", "pkv_attention_decode",
                  "pkv_attention_decode_shared", "pkv_attention_prefill", "pkv_kv_write_fp8",
-                 "pkv_attention_decode_fp8", "pkv_block_copy_fp8", "pkv_block_transfer_fp8",
+                 "pkv_attention_decode_fp8", "pkv_attention_prefill_fp8", "pkv_block_copy_fp8",
+                 "pkv_block_transfer_fp8",
                  "pkv_check_device_errors"):
         getattr(lib, name).restype = ctypes.c_int
     _LIB = lib
@@ -404,6 +408,32 @@ def pkv_attention_decode_fp8(out: torch.Tensor, q: torch.Tensor, k_cache: torch.
         _ptr(out), _DTYPES[out.dtype], _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
         _ptr(v_scale), ctypes.byref(desc), _ptr(block_tables), mb, _ptr(seq_lens), B, Hq,
         float(scale), partition_tokens, _ptr(workspace), wbytes, _stream()))
+    return out
+
+
+def pkv_attention_prefill_fp8(out: torch.Tensor, q: torch.Tensor, query_start: torch.Tensor,
+                              k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: torch.Tensor,
+                              v_scale: torch.Tensor, block_tables: torch.Tensor,
+                              seq_lens: torch.Tensor, scale: float) -> torch.Tensor:
+    """Prefill attention over FP8 pools into ``out`` ``[T, Hq, 128]``; ``q`` is bf16.  Returns ``out``."""
+    desc = _desc_fp8(k_cache, v_cache, k_scale, v_scale)
+    _need(q, "q", dtype=torch.bfloat16, ndim=3)
+    _need(out, "out", ndim=3)
+    if out.dtype not in _DTYPES:
+        raise TypeError("out must be float32 or bfloat16")
+    _need(query_start, "query_start", dtype=torch.int32, ndim=1)
+    _need(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _need(seq_lens, "seq_lens", dtype=torch.int32, ndim=1)
+    T, Hq, D = q.shape
+    B = seq_lens.shape[0]
+    if tuple(out.shape) != (T, Hq, D) or D != desc.head_dim:
+        raise ValueError("out/q shapes do not match [num_tokens, Hq, head_dim]")
+    if block_tables.shape[0] != B or query_start.shape[0] != B + 1:
+        raise ValueError("block_tables must have B rows and query_start B + 1 entries")
+    _check(load_library().pkv_attention_prefill_fp8(
+        _ptr(out), _DTYPES[out.dtype], _ptr(q), T, _ptr(query_start), _ptr(k_cache), _ptr(v_cache),
+        _ptr(k_scale), _ptr(v_scale), ctypes.byref(desc), _ptr(block_tables),
+        block_tables.shape[1], _ptr(seq_lens), B, Hq, float(scale), _stream()))
     return out
 
 

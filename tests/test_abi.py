@@ -348,3 +348,25 @@ def test_fp8_workspace_matches_bf16(lib):
         w8 = lib.pkv_attention_workspace_bytes(ctypes.byref(desc(dtype=FP8)), B, 32, 256, part)
         assert w8 == w16 > 0, (B, part, w8, w16)
     assert decode_fp8(lib, ws=P(0)) == WORKSPACE
+
+
+def test_fp8_prefill_validation(lib):
+    d8, d16 = desc(dtype=FP8), desc()
+
+    def prefill_fp8(d, **kw):
+        a = dict(out=P(), q=P(), T=64, qs=P(), ks=P(), vs=P(), B=4, Hq=32, scale=0.088)
+        a.update(kw)
+        return lib.pkv_attention_prefill_fp8(a["out"], 0, a["q"], a["T"], a["qs"], P(), P(),
+                                             a["ks"], a["vs"], ctypes.byref(d), P(), 32, P(),
+                                             a["B"], a["Hq"], a["scale"], P(0))
+
+    assert prefill_fp8(d8, B=0) == OK
+    assert prefill_fp8(d16) == UNSUPPORTED            # bf16 pools go to pkv_attention_prefill
+    assert prefill_fp8(desc(d=64, dtype=FP8)) == UNSUPPORTED
+    assert prefill_fp8(d8, ks=P(0)) == INVALID
+    assert "k_scale" in ops.pkv_last_error()
+    assert prefill_fp8(d8, Hq=24) == UNSUPPORTED
+    # and the bf16 prefill takes no FP8 pools
+    assert lib.pkv_attention_prefill(P(), 0, P(), 64, P(), P(), P(), ctypes.byref(d8), P(), 32,
+                                     P(), 4, 32, 0.088, P(0)) == UNSUPPORTED
+    assert "pkv_attention_prefill_fp8" in ops.pkv_last_error()
