@@ -306,8 +306,13 @@ class Step:
             self.ops.pkv_kv_write_fp8(self.k_new, self.v_new, self.slots, kc, vc, ks, vs)
             if ev:
                 ev[2].record()
-            self.ops.pkv_attention_decode_fp8(self.out, self.q, kc, vc, ks, vs, self.bt, self.sl,
-                                              self.scale, self.part, self.ws)
+            if self.groups is None:
+                self.ops.pkv_attention_decode_fp8(self.out, self.q, kc, vc, ks, vs, self.bt,
+                                                  self.sl, self.scale, self.part, self.ws)
+            else:
+                self.ops.pkv_attention_decode_shared_fp8(self.out, self.q, kc, vc, ks, vs,
+                                                         self.bt, self.sl, self.scale,
+                                                         *self.groups, workspace=self.ws)
             if ev:
                 ev[3].record()
             return
@@ -380,24 +385,52 @@ def fp8_step_state(torch, ops, w, npools, partition_tokens):
                 partition_tokens, fp8_scales=(ks, vs))
 
 
-def sharing_step_state(torch, ops, ws, final, partition_tokens, shared=False):
+def sharing_step_state(torch, ops, ws, final, partition_tokens, shared=False, fp8=False):
     """Pool of the prefix-sharing workload at its first divergent step (with its
     copy-on-write copies) or at its last step; returns (Step, seq_lens).  With
     `shared` the step decodes with pkv_attention_decode_shared, the groups
-    taken from the block manager."""
-    from paged_kv_cache_330_amd.workloads import empty_device_caches, torch_tensor
+    taken from the block manager.  With `fp8` the pools hold E4M3 codes: each
+    prompt block's scales are its own max-abs / 448, every other block's the
+    prompts' overall max-abs / 448 (the tails are drawn from the same
+    distribution)."""
+    import numpy as np
+    from paged_kv_cache_330_amd.workloads import (empty_device_caches, fp8_block_scales,
+                                                  torch_tensor)
     dev = "cuda"
-    kc, vc = empty_device_caches(ws.num_blocks, ws.block_size, ws.num_kv_heads, ws.head_dim,
-                                 "bf16", dev, fill="zero")
     pk, pv, ps = ws.prefill()
-    ops.pkv_kv_write(torch_tensor(pk, "bf16", dev), torch_tensor(pv, "bf16", dev),
-                     torch.from_numpy(ps).to(dev), kc, vc)
+    if fp8:
+        shape = (ws.num_blocks, ws.block_size, ws.num_kv_heads, ws.head_dim)
+        kc = torch.zeros(shape, dtype=torch.uint8, device=dev)
+        vc = torch.zeros(shape, dtype=torch.uint8, device=dev)
+        sc = []
+        for s in fp8_block_scales(pk, pv, ps, ws.num_blocks, ws.block_size):
+            s[np.isnan(s)] = np.nanmax(s)
+            sc.append(torch.from_numpy(s).to(dev))
+        fp8_scales = tuple(sc)
+
+        def write(k, v, slots):
+            ops.pkv_kv_write_fp8(k, v, slots, kc, vc, *fp8_scales)
+
+        def copy(pairs):
+            ops.pkv_block_copy_fp8(kc, vc, *fp8_scales, pairs)
+    else:
+        kc, vc = empty_device_caches(ws.num_blocks, ws.block_size, ws.num_kv_heads, ws.head_dim,
+                                     "bf16", dev, fill="zero")
+        fp8_scales = None
+
+        def write(k, v, slots):
+            ops.pkv_kv_write(k, v, slots, kc, vc)
+
+        def copy(pairs):
+            ops.pkv_block_copy(kc, vc, pairs)
+    write(torch_tensor(pk, "bf16", dev), torch_tensor(pv, "bf16", dev),
+          torch.from_numpy(ps).to(dev))
     st = ws.next_step()
     while final and ws.steps_done < ws.tail_len:  # apply every step but the last
         if len(st.copy_pairs):
-            ops.pkv_block_copy(kc, vc, torch.from_numpy(st.copy_pairs).to(dev))
-        ops.pkv_kv_write(torch_tensor(st.k_new, "bf16", dev), torch_tensor(st.v_new, "bf16", dev),
-                         torch.from_numpy(st.slot_mapping).to(dev), kc, vc)
+            copy(torch.from_numpy(st.copy_pairs).to(dev))
+        write(torch_tensor(st.k_new, "bf16", dev), torch_tensor(st.v_new, "bf16", dev),
+              torch.from_numpy(st.slot_mapping).to(dev))
         st = ws.next_step()
     pairs = torch.from_numpy(st.copy_pairs).to(dev) if len(st.copy_pairs) else None
     groups = None
@@ -408,7 +441,7 @@ def sharing_step_state(torch, ops, ws, final, partition_tokens, shared=False):
                 torch.from_numpy(st.block_tables).to(dev), torch.from_numpy(st.seq_lens).to(dev),
                 torch_tensor(st.k_new, "bf16", dev), torch_tensor(st.v_new, "bf16", dev),
                 torch.from_numpy(st.slot_mapping).to(dev), pairs, float(ws.scale),
-                partition_tokens, groups)
+                partition_tokens, groups, fp8_scales=fp8_scales)
     return step, st.seq_lens
 
 
@@ -539,25 +572,37 @@ def report_all(torch, ops, args):
     swap_report(torch, ops)
     # the prefix-sharing workload as stated (4 prompts x 8 samples) at both
     # block sizes, first divergent and last step; then 64 prompts x 8 samples
-    # (512 sequences, 1.07 GB of unique K/V, 4.8 GB read by the plain decode)
+    # (512 sequences, 1.07 GB of unique K/V, 4.8 GB read by the plain decode),
+    # also over FP8 pools
     cases = [(4, bs, final) for bs in (8, 16) for final in (False, True)] + [(64, 16, True)]
     for prompts, bs, final in cases:
-        for shared in (False, True):
+        kinds = [(False, False), (True, False)]
+        if prompts == 64:
+            kinds += [(False, True), (True, True)]
+        for shared, fp8 in kinds:
             ws = PrefixSharingWorkload(prefix_len=args.prefix, block_size=bs, prompts=prompts)
             st, lens = sharing_step_state(torch, ops, ws, final, args.partition_tokens,
-                                          shared)
+                                          shared, fp8)
             wall, t_copy, t_write, t_attn = time_steps(torch, st, steps, warmup)
             n_pairs = 0 if st.pairs is None else int(st.pairs.shape[0])
             name = "prefix_sharing_shared_decode" if shared else "prefix_sharing"
+            es = 1 if fp8 else 2
+            extra = {"prompts": prompts, "samples": ws.samples, "prefix": args.prefix,
+                     "step": ws.steps_done, "seed": ws.seed}
+            if fp8:
+                name += "_fp8_e4m3"
+                extra["kv_dtype"] = "fp8_e4m3"
             res, kv, _ = summary(
-                name, {"prompts": prompts, "samples": ws.samples, "prefix": args.prefix,
-                       "step": ws.steps_done, "seed": ws.seed},
-                lens, ws.num_seqs, ws.num_q_heads, ws.num_kv_heads, ws.head_dim, bs, steps,
-                wall, t_copy, t_write, t_attn, n_pairs)
+                name, extra, lens, ws.num_seqs, ws.num_q_heads, ws.num_kv_heads, ws.head_dim, bs,
+                steps, wall, t_copy, t_write, t_attn, n_pairs, es=es)
+            if fp8:  # bf16 K/V in, 1-byte codes out, slots and scales read
+                B, rowe = ws.num_seqs, ws.num_kv_heads * ws.head_dim
+                wb = B * rowe * 2 * (2 + 1) + 8 * B + 2 * 4 * B * ws.num_kv_heads
+                res["write_gbps"] = round(wb / (statistics.median(t_write) * 1e-3) / 1e9, 2)
             # K/V bytes held once: the prompts' prefixes and every sample's own tail
             unique = (ws.prompts * ws.prefix_len
                       + ws.num_seqs * (int(lens[0]) - ws.prefix_len)) \
-                * ws.num_kv_heads * ws.head_dim * 2 * 2
+                * ws.num_kv_heads * ws.head_dim * 2 * es
             res["unique_kv_bytes"] = unique
             res["unique_kv_gbps"] = round(
                 unique / (res["t_attn_us"]["median"] * 1e-6) / 1e9, 2)

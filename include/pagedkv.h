@@ -177,9 +177,10 @@ int pkv_attention_decode(void* out, int32_t out_dtype, const void* q,
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Bytes of device workspace pkv_attention_decode_shared needs (0 for arguments
+ * Bytes of device workspace pkv_attention_decode_shared (bf16 descriptor) or
+ * pkv_attention_decode_shared_fp8 (FP8 descriptor) needs: 0 for arguments
  * that call would reject, with pkv_last_error() saying why, and for
- * num_seqs == 0).  Host-known sizes only.
+ * num_seqs == 0.  Host-known sizes only.
  */
 size_t pkv_attention_shared_workspace_bytes(const pkv_cache_desc* cache, int32_t num_seqs,
                                             int32_t num_q_heads, int32_t num_groups);
@@ -195,7 +196,8 @@ size_t pkv_attention_shared_workspace_bytes(const pkv_cache_desc* cache, int32_t
  * shared block once for the whole group instead of once per member.
  *
  * All arguments shared with pkv_attention_decode mean the same; the pools
- * must be PKV_BF16 with head_dim 128, and num_seqs <= 2048.
+ * must be PKV_BF16 with head_dim 128 (FP8 pools: the _fp8 variant), and
+ * num_seqs <= 2048.
  *   group_offsets [num_groups + 1] int32: the members of group g are
  *                 group_seqs[group_offsets[g] .. group_offsets[g + 1]);
  *                 group_offsets[0] == 0, nondecreasing, last <= num_seqs.
@@ -316,6 +318,26 @@ int pkv_attention_prefill_fp8(void* out, int32_t out_dtype, const void* q, int64
                               const pkv_cache_desc* cache, const int32_t* block_tables,
                               int32_t max_blocks_per_seq, const int32_t* seq_lens,
                               int32_t num_seqs, int32_t num_q_heads, float scale, void* stream);
+
+/*
+ * Shared-prefix decode over FP8 pools: the result pkv_attention_decode_shared
+ * gives for pools holding the dequantized values scale * value(code) (q is
+ * bf16), which is also what pkv_attention_decode_fp8 gives on the same
+ * arguments.  Every other argument, the group description and the workspace
+ * (sized by pkv_attention_shared_workspace_bytes with the FP8 descriptor)
+ * included, means what it means for pkv_attention_decode_shared, and is
+ * checked the same way.  Blocks shared by a group share their scales too,
+ * since a scale belongs to a physical block.  Scales are used as given.
+ */
+int pkv_attention_decode_shared_fp8(void* out, int32_t out_dtype, const void* q,
+                                    const void* k_cache, const void* v_cache,
+                                    const float* k_scale, const float* v_scale,
+                                    const pkv_cache_desc* cache, const int32_t* block_tables,
+                                    int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                    int32_t num_seqs, int32_t num_q_heads, float scale,
+                                    const int32_t* group_offsets, const int32_t* group_seqs,
+                                    const int32_t* group_lens, int32_t num_groups,
+                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pkv_block_copy for FP8 pools: each pair copies the K and V codes of the

@@ -205,8 +205,9 @@ int make_shared_plan(const pkv_cache_desc* cache, int32_t num_seqs, int32_t num_
                      int32_t max_blocks_per_seq, int32_t num_groups, SharedPlan* p) {
   Plan base;
   PKV_TRY(make_plan(cache, num_seqs, num_q_heads, max_blocks_per_seq, 0, &base));
-  if (cache->dtype != PKV_BF16 || cache->head_dim != 128)
-    return fail(PKV_ERR_UNSUPPORTED, "shared-prefix decode needs bf16 pools with head_dim 128");
+  if ((cache->dtype != PKV_BF16 && cache->dtype != PKV_FP8_E4M3) || cache->head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED,
+                "shared-prefix decode needs bf16 or FP8 pools with head_dim 128");
   const int group = num_q_heads / cache->num_kv_heads;
   if (group != 1 && group != 2 && group != 4 && group != 8)
     return fail(PKV_ERR_UNSUPPORTED, "query group %d is not 1, 2, 4 or 8", group);
@@ -418,42 +419,6 @@ size_t pkv_attention_shared_workspace_bytes(const pkv_cache_desc* cache, int32_t
   return p.workspace;
 }
 
-int pkv_attention_decode_shared(void* out, int32_t out_dtype, const void* q, const void* k_cache,
-                                const void* v_cache, const pkv_cache_desc* cache,
-                                const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
-                                float scale, const int32_t* group_offsets,
-                                const int32_t* group_seqs, const int32_t* group_lens,
-                                int32_t num_groups, void* workspace, size_t workspace_bytes,
-                                void* stream) {
-  g_last_error.clear();
-  SharedPlan plan;
-  PKV_TRY(make_shared_plan(cache, num_seqs, num_q_heads, max_blocks_per_seq, num_groups, &plan));
-  PKV_TRY(check_decode_scalars(cache, num_q_heads, out_dtype, scale));
-  if (num_seqs == 0) return PKV_OK;
-  pkv::SharedArgs sa{};
-  PKV_TRY(fill_decode_args(out, out_dtype, q, k_cache, v_cache, cache, block_tables,
-                           max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, scale, &sa.d));
-  if (num_groups > 0) {
-    PKV_TRY(check_ptr(group_offsets, 4, "group_offsets"));
-    PKV_TRY(check_ptr(group_seqs, 4, "group_seqs"));
-    PKV_TRY(check_ptr(group_lens, 4, "group_lens"));
-  }
-  PKV_TRY(attach_workspace(workspace, workspace_bytes, plan.workspace, plan.layout, &sa.d));
-  PKV_TRY(error_word(&sa.d.err));
-  sa.d.slices = plan.slices;
-  sa.group_offsets = group_offsets;
-  sa.group_seqs = group_seqs;
-  sa.group_lens = group_lens;
-  sa.num_groups = num_groups;
-  sa.min_chunks = PKV_SHARED_MIN_CHUNKS;
-  sa.prefix_rows = plan.prefix_rows;
-  hipError_t e = pkv::launch_shared_decode(sa, cache->block_size,
-                                           num_q_heads / cache->num_kv_heads,
-                                           static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? PKV_OK : hip_fail(e, "attention_decode_shared launch");
-}
-
 }  // extern "C"
 
 namespace {
@@ -500,9 +465,86 @@ int prefill_common(void* out, int32_t out_dtype, const void* q, int64_t num_toke
   return e == hipSuccess ? PKV_OK : hip_fail(e, "attention_prefill launch");
 }
 
+// Both shared-prefix decode calls: FP8 pools bring their scales.
+int shared_common(void* out, int32_t out_dtype, const void* q, const void* k_cache,
+                  const void* v_cache, const float* k_scale, const float* v_scale,
+                  const pkv_cache_desc* cache, const int32_t* block_tables,
+                  int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                  int32_t num_q_heads, float scale, const int32_t* group_offsets,
+                  const int32_t* group_seqs, const int32_t* group_lens, int32_t num_groups,
+                  void* workspace, size_t workspace_bytes, void* stream, bool fp8) {
+  SharedPlan plan;
+  PKV_TRY(make_shared_plan(cache, num_seqs, num_q_heads, max_blocks_per_seq, num_groups, &plan));
+  if (fp8) {
+    PKV_TRY(check_fp8(cache, "pkv_attention_decode_shared_fp8"));
+  } else {
+    PKV_TRY(check_not_fp8(cache, "pkv_attention_decode_shared"));
+  }
+  PKV_TRY(check_decode_scalars(cache, num_q_heads, out_dtype, scale));
+  if (num_seqs == 0) return PKV_OK;
+  pkv::SharedArgs sa{};
+  PKV_TRY(fill_decode_args(out, out_dtype, q, k_cache, v_cache, cache, block_tables,
+                           max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, scale, &sa.d));
+  if (fp8) {
+    PKV_TRY(check_ptr(k_scale, 4, "k_scale"));
+    PKV_TRY(check_ptr(v_scale, 4, "v_scale"));
+    sa.d.k_scale = k_scale;
+    sa.d.v_scale = v_scale;
+  }
+  if (num_groups > 0) {
+    PKV_TRY(check_ptr(group_offsets, 4, "group_offsets"));
+    PKV_TRY(check_ptr(group_seqs, 4, "group_seqs"));
+    PKV_TRY(check_ptr(group_lens, 4, "group_lens"));
+  }
+  PKV_TRY(attach_workspace(workspace, workspace_bytes, plan.workspace, plan.layout, &sa.d));
+  PKV_TRY(error_word(&sa.d.err));
+  sa.d.slices = plan.slices;
+  sa.group_offsets = group_offsets;
+  sa.group_seqs = group_seqs;
+  sa.group_lens = group_lens;
+  sa.num_groups = num_groups;
+  sa.min_chunks = PKV_SHARED_MIN_CHUNKS;
+  sa.prefix_rows = plan.prefix_rows;
+  hipError_t e = pkv::launch_shared_decode(sa, cache->block_size,
+                                           num_q_heads / cache->num_kv_heads,
+                                           static_cast<hipStream_t>(stream), fp8);
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "attention_decode_shared launch");
+}
+
 }  // namespace
 
 extern "C" {
+
+int pkv_attention_decode_shared(void* out, int32_t out_dtype, const void* q, const void* k_cache,
+                                const void* v_cache, const pkv_cache_desc* cache,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                float scale, const int32_t* group_offsets,
+                                const int32_t* group_seqs, const int32_t* group_lens,
+                                int32_t num_groups, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  g_last_error.clear();
+  return shared_common(out, out_dtype, q, k_cache, v_cache, nullptr, nullptr, cache, block_tables,
+                       max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, scale, group_offsets,
+                       group_seqs, group_lens, num_groups, workspace, workspace_bytes, stream,
+                       false);
+}
+
+int pkv_attention_decode_shared_fp8(void* out, int32_t out_dtype, const void* q,
+                                    const void* k_cache, const void* v_cache,
+                                    const float* k_scale, const float* v_scale,
+                                    const pkv_cache_desc* cache, const int32_t* block_tables,
+                                    int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                    int32_t num_seqs, int32_t num_q_heads, float scale,
+                                    const int32_t* group_offsets, const int32_t* group_seqs,
+                                    const int32_t* group_lens, int32_t num_groups,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  return shared_common(out, out_dtype, q, k_cache, v_cache, k_scale, v_scale, cache, block_tables,
+                       max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, scale, group_offsets,
+                       group_seqs, group_lens, num_groups, workspace, workspace_bytes, stream,
+                       true);
+}
 
 int pkv_attention_prefill(void* out, int32_t out_dtype, const void* q, int64_t num_tokens,
                           const int32_t* query_start, const void* k_cache, const void* v_cache,

@@ -1,5 +1,6 @@
 // Decode-step attention for groups of sequences that share a prefix of their
-// KV cache, bf16 pools with head_dim 128, on the matrix cores of gfx950.
+// KV cache, bf16 or E4M3 pools with head_dim 128, on the matrix cores of
+// gfx950 (E4M3 tiles are widened to bf16 on load, as in the plain decode).
 //
 // What is shared ("PagedAttention 动态内存分页", section "写时复制与内存共享";
 // "Paged KV" wiki, section "支持 Prefix Cache"): sequences forked from one
@@ -80,7 +81,7 @@ __device__ __forceinline__ void store_columns(const DecodeArgs& a, MfmaState<NS>
 }
 
 // Workgroup (kv-head group, slice); wave w owns kv head blockIdx.x * KH + w.
-template <int G, int BS, int TC>
+template <int G, int BS, int TC, bool F8>
 __global__ __launch_bounds__(kMaxWaves * 64) void decode_shared_kernel(SharedArgs sa) {
   static_assert(16 % G == 0, "group must divide 16");
   static_assert(TC == 1, "V tiles hold one 16-row chunk per wave (LDS is nearly full)");
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_shared_kernel(SharedArg
       }
       MfmaState<kSharedSets> ps;
       ps.reset();
-      attend_table<BS, TC, true>(a, s_bt, k_lds, v_lds,
+      attend_table<BS, TC, true, F8>(a, s_bt, k_lds, v_lds,
                                  a.block_tables + (int64_t)lead * a.max_blocks_per_seq,
                                  q + ((int64_t)lead * a.num_q_heads + kvh * G) * kD, kvh,
                                  (c - cs) * 16, (c_end - cs) * 16, qop, ps,
@@ -258,8 +259,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_shared_kernel(SharedArg
       load_query<G>(a, b, kvh, col, qr, qop);
       WaveState<G> ws;
       ws.reset();
-      attend_range<G, BS, TC>(a, s_bt, k_lds, v_lds, b, kvh, T + (c - cs) * 16,
-                              min(T + (c_end - cs) * 16, L), qop, ws);
+      attend_range<G, BS, TC, F8>(a, s_bt, k_lds, v_lds, b, kvh, T + (c - cs) * 16,
+                                  min(T + (c_end - cs) * 16, L), qop, ws);
       Sink sink{nullptr, nullptr, nullptr, 0, 0};
       if (!(T == 0 && c == cs && c_end == ce))
         sink = Sink{a.ws_acc, a.ws_max, a.ws_sum,
@@ -313,16 +314,16 @@ __global__ __launch_bounds__(256) void shared_merge_kernel(SharedArgs sa) {
   store_out(a, o + 1, num1 / den);
 }
 
-template <int G>
+template <int G, bool F8>
 hipError_t launch_shared_g(const SharedArgs& a, int block_size, int kh, hipStream_t s) {
   constexpr int TC = 1;  // one chunk per tile: the V tiles are sized for 16 rows
   const dim3 grid(a.d.num_kv_heads / kh, a.d.slices);
   const dim3 block(kh * 64);
   switch (block_size) {
-    case 8: decode_shared_kernel<G, 8, TC><<<grid, block, 0, s>>>(a); break;
-    case 16: decode_shared_kernel<G, 16, TC><<<grid, block, 0, s>>>(a); break;
-    case 32: decode_shared_kernel<G, 32, TC><<<grid, block, 0, s>>>(a); break;
-    case 64: decode_shared_kernel<G, 64, TC><<<grid, block, 0, s>>>(a); break;
+    case 8: decode_shared_kernel<G, 8, TC, F8><<<grid, block, 0, s>>>(a); break;
+    case 16: decode_shared_kernel<G, 16, TC, F8><<<grid, block, 0, s>>>(a); break;
+    case 32: decode_shared_kernel<G, 32, TC, F8><<<grid, block, 0, s>>>(a); break;
+    case 64: decode_shared_kernel<G, 64, TC, F8><<<grid, block, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
@@ -333,16 +334,21 @@ hipError_t launch_shared_g(const SharedArgs& a, int block_size, int kh, hipStrea
 
 }  // namespace
 
-hipError_t launch_shared_decode(const SharedArgs& a, int block_size, int group, hipStream_t s) {
+hipError_t launch_shared_decode(const SharedArgs& a, int block_size, int group, hipStream_t s,
+                                bool fp8) {
   if (a.d.num_seqs < 1 || a.d.num_seqs > kMaxBalancedSeqs || a.num_groups < 0 ||
       a.num_groups > a.d.num_seqs)
     return hipErrorInvalidValue;
   const int kh = mfma_waves_per_group(a.d.num_kv_heads);
   switch (group) {
-    case 1: return launch_shared_g<1>(a, block_size, kh, s);
-    case 2: return launch_shared_g<2>(a, block_size, kh, s);
-    case 4: return launch_shared_g<4>(a, block_size, kh, s);
-    case 8: return launch_shared_g<8>(a, block_size, kh, s);
+    case 1: return fp8 ? launch_shared_g<1, true>(a, block_size, kh, s)
+                         : launch_shared_g<1, false>(a, block_size, kh, s);
+    case 2: return fp8 ? launch_shared_g<2, true>(a, block_size, kh, s)
+                         : launch_shared_g<2, false>(a, block_size, kh, s);
+    case 4: return fp8 ? launch_shared_g<4, true>(a, block_size, kh, s)
+                         : launch_shared_g<4, false>(a, block_size, kh, s);
+    case 8: return fp8 ? launch_shared_g<8, true>(a, block_size, kh, s)
+                         : launch_shared_g<8, false>(a, block_size, kh, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -192,7 +192,8 @@ struct SharedArgs {
   int64_t prefix_rows;           // partial rows of prefix pieces; tail rows follow
 };
 
-hipError_t launch_shared_decode(const SharedArgs& a, int block_size, int group, hipStream_t stream);
+hipError_t launch_shared_decode(const SharedArgs& a, int block_size, int group, hipStream_t stream,
+                                bool fp8 = false);
 
 // Prefill attention (attention_prefill.hip): new tokens of sequence b are the
 // query rows query_start[b] .. query_start[b + 1] - 1 of d.q and d.out.

@@ -30,6 +30,7 @@ __all__ = [
     "pkv_kv_write_fp8",
     "pkv_attention_decode_fp8",
     "pkv_attention_prefill_fp8",
+    "pkv_attention_decode_shared_fp8",
     "pkv_block_copy_fp8",
     "pkv_block_transfer_fp8",
     "pkv_check_device_errors",
@@ -98,6 +99,8 @@ def load_library() -> ctypes.CDLL:
                                              ctypes.c_float, I32, P, SZ, P]
     lib.pkv_attention_prefill_fp8.argtypes = [P, I32, P, I64, P, P, P, P, P, D, P, I32, P, I32,
                                               I32, ctypes.c_float, P]
+    lib.pkv_attention_decode_shared_fp8.argtypes = [P, I32, P, P, P, P, P, D, P, I32, P, I32, I32,
+                                                    ctypes.c_float, P, P, P, I32, P, SZ, P]
     lib.pkv_block_copy_fp8.argtypes = [P, P, P, P, D, P, I64, P]
     lib.pkv_block_transfer_fp8.argtypes = [P, P, P, P, D, P, P, P, P, D, P, I64, P]
     lib.pkv_last_error.restype = ctypes.c_char_p
@@ -105,7 +108,7 @@ def load_library() -> ctypes.CDLL:
     for name in ("pkv_kv_write", "pkv_block_copy", "pkv_block_transfer", "pkv_attention_decode",
                  "pkv_attention_decode_shared", "pkv_attention_prefill", "pkv_kv_write_fp8",
                  "pkv_attention_decode_fp8", "pkv_attention_prefill_fp8", "pkv_block_copy_fp8",
-                 "pkv_block_transfer_fp8",
+                 "pkv_block_transfer_fp8", "pkv_attention_decode_shared_fp8",
                  "pkv_check_device_errors"):
         getattr(lib, name).restype = ctypes.c_int
     _LIB = lib
@@ -274,28 +277,27 @@ def pkv_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tens
 
 def pkv_attention_shared_workspace_bytes(k_cache: torch.Tensor, v_cache: torch.Tensor,
                                          num_seqs: int, num_q_heads: int, num_groups: int) -> int:
-    """Workspace bytes ``pkv_attention_decode_shared`` needs for these pools and sizes."""
-    desc = _desc(k_cache, v_cache)
+    """Workspace bytes ``pkv_attention_decode_shared`` (bf16 pools) or
+    ``pkv_attention_decode_shared_fp8`` (uint8 / float8_e4m3fn pools) needs."""
+    if k_cache.dtype in _FP8_DTYPES:
+        _need(k_cache, "k_cache", ndim=4)
+        nb, bs, hkv, d = k_cache.shape
+        desc = CacheDesc(nb, bs, hkv, d, PKV_FP8_E4M3)
+    else:
+        desc = _desc(k_cache, v_cache)
     return int(load_library().pkv_attention_shared_workspace_bytes(
         ctypes.byref(desc), num_seqs, num_q_heads, num_groups))
 
 
-def pkv_attention_decode_shared(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
-                                v_cache: torch.Tensor, block_tables: torch.Tensor,
-                                seq_lens: torch.Tensor, scale: float,
-                                group_offsets: Optional[torch.Tensor],
-                                group_seqs: Optional[torch.Tensor],
-                                group_lens: Optional[torch.Tensor],
-                                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Decode attention for sequences that share prefixes; returns ``out``.
-
-    The result is that of ``pkv_attention_decode`` on the same arguments.
-    ``group_offsets`` ``[G + 1]``, ``group_seqs`` and ``group_lens`` ``[G]`` are
-    int32 GPU tensors describing the groups (all three may be ``None`` for no
-    group); ``workspace`` is allocated through torch when not given.
-    """
-    desc = _desc(k_cache, v_cache)
-    _need(q, "q", dtype=k_cache.dtype, ndim=3)
+def _decode_shared(out, q, k_cache, v_cache, scales, block_tables, seq_lens, scale,
+                   group_offsets, group_seqs, group_lens, workspace):
+    """Checks and marshals both shared-prefix calls; ``scales`` is None or (k, v)."""
+    if scales is None:
+        desc = _desc(k_cache, v_cache)
+        _need(q, "q", dtype=k_cache.dtype, ndim=3)
+    else:
+        desc = _desc_fp8(k_cache, v_cache, *scales)
+        _need(q, "q", dtype=torch.bfloat16, ndim=3)
     _need(out, "out", ndim=3)
     if out.dtype not in _DTYPES:
         raise TypeError("out must be float32 or bfloat16")
@@ -319,17 +321,56 @@ def pkv_attention_decode_shared(out: torch.Tensor, q: torch.Tensor, k_cache: tor
         if group_offsets.shape[0] != ng + 1:
             raise ValueError("group_offsets must have len(group_lens) + 1 entries")
     mb = block_tables.shape[1]
-    need = int(load_library().pkv_attention_shared_workspace_bytes(ctypes.byref(desc), B, Hq, ng))
+    lib = load_library()
+    need = int(lib.pkv_attention_shared_workspace_bytes(ctypes.byref(desc), B, Hq, ng))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if workspace is not None:
         _need(workspace, "workspace")
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(load_library().pkv_attention_decode_shared(
-        _ptr(out), _DTYPES[out.dtype], _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
-        _ptr(block_tables), mb, _ptr(seq_lens), B, Hq, float(scale), _ptr(group_offsets),
-        _ptr(group_seqs), _ptr(group_lens), ng, _ptr(workspace), wbytes, _stream()))
+    head = (_ptr(out), _DTYPES[out.dtype], _ptr(q), _ptr(k_cache), _ptr(v_cache))
+    tail = (ctypes.byref(desc), _ptr(block_tables), mb, _ptr(seq_lens), B, Hq, float(scale),
+            _ptr(group_offsets), _ptr(group_seqs), _ptr(group_lens), ng, _ptr(workspace), wbytes,
+            _stream())
+    if scales is None:
+        _check(lib.pkv_attention_decode_shared(*head, *tail))
+    else:
+        _check(lib.pkv_attention_decode_shared_fp8(*head, _ptr(scales[0]), _ptr(scales[1]), *tail))
     return out
+
+
+def pkv_attention_decode_shared(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                                v_cache: torch.Tensor, block_tables: torch.Tensor,
+                                seq_lens: torch.Tensor, scale: float,
+                                group_offsets: Optional[torch.Tensor],
+                                group_seqs: Optional[torch.Tensor],
+                                group_lens: Optional[torch.Tensor],
+                                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode attention for sequences that share prefixes; returns ``out``.
+
+    The result is that of ``pkv_attention_decode`` on the same arguments.
+    ``group_offsets`` ``[G + 1]``, ``group_seqs`` and ``group_lens`` ``[G]`` are
+    int32 GPU tensors describing the groups (all three may be ``None`` for no
+    group); ``workspace`` is allocated through torch when not given.
+    """
+    return _decode_shared(out, q, k_cache, v_cache, None, block_tables, seq_lens, scale,
+                          group_offsets, group_seqs, group_lens, workspace)
+
+
+def pkv_attention_decode_shared_fp8(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                                    v_cache: torch.Tensor, k_scale: torch.Tensor,
+                                    v_scale: torch.Tensor, block_tables: torch.Tensor,
+                                    seq_lens: torch.Tensor, scale: float,
+                                    group_offsets: Optional[torch.Tensor],
+                                    group_seqs: Optional[torch.Tensor],
+                                    group_lens: Optional[torch.Tensor],
+                                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``pkv_attention_decode_shared`` over FP8 pools with their per-block scales; ``q`` is bf16.
+
+    The result is that of ``pkv_attention_decode_fp8`` on the same arguments.
+    """
+    return _decode_shared(out, q, k_cache, v_cache, (k_scale, v_scale), block_tables, seq_lens,
+                          scale, group_offsets, group_seqs, group_lens, workspace)
 
 
 def pkv_attention_prefill(out: torch.Tensor, q: torch.Tensor, query_start: torch.Tensor,

@@ -370,3 +370,32 @@ def test_fp8_prefill_validation(lib):
     assert lib.pkv_attention_prefill(P(), 0, P(), 64, P(), P(), P(), ctypes.byref(d8), P(), 32,
                                      P(), 4, 32, 0.088, P(0)) == UNSUPPORTED
     assert "pkv_attention_prefill_fp8" in ops.pkv_last_error()
+
+
+def shared_fp8(lib, **kw):
+    a = dict(out=P(), q=P(), ks=P(), vs=P(), desc=desc(dtype=FP8), B=32, Hq=32, scale=0.088,
+             go=P(), ng=4, ws=P(), wsb=1 << 30)
+    a.update(kw)
+    return lib.pkv_attention_decode_shared_fp8(
+        a["out"], 0, a["q"], P(), P(), a["ks"], a["vs"], ctypes.byref(a["desc"]), P(), 32, P(),
+        a["B"], a["Hq"], a["scale"], a["go"], P(), P(), a["ng"], a["ws"], a["wsb"], P(0))
+
+
+def test_fp8_shared_prefix_validation(lib):
+    d8 = desc(dtype=FP8)
+    # same schedule, hence the same workspace, as over bf16 pools
+    for B, hq, ng in ((32, 32, 4), (2048, 64, 100), (1, 8, 0)):
+        assert shared_ws(lib, d8, B, hq, ng) == shared_ws(lib, desc(), B, hq, ng) > 0
+    assert shared_fp8(lib, B=0, ng=0, out=P(0), q=P(0)) == OK       # no-op
+    assert shared_fp8(lib, desc=desc()) == UNSUPPORTED              # bf16 pools: the plain call
+    assert "FP8" in ops.pkv_last_error()
+    assert shared_fp8(lib, desc=desc(d=64, dtype=FP8)) == UNSUPPORTED
+    assert shared_fp8(lib, ks=P(0)) == INVALID
+    assert "k_scale" in ops.pkv_last_error()
+    assert shared_fp8(lib, vs=P(FAKE + 2)) == INVALID
+    assert shared_fp8(lib, go=P(0)) == INVALID
+    assert shared_fp8(lib, Hq=24) == UNSUPPORTED
+    assert shared_fp8(lib, ws=P(0)) == WORKSPACE
+    # and the bf16 shared call takes no FP8 pools
+    assert shared(lib, desc=d8) == UNSUPPORTED
+    assert "pkv_attention_decode_shared_fp8" in ops.pkv_last_error()
