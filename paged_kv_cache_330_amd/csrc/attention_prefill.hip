@@ -18,11 +18,12 @@
 // (16 n + col) / G of the wave, head col % G), so Q.K^T and P.V are dense
 // products of each K/V tile with 32 queries per wave.  The item streams its
 // key range, tokens 0 .. (position of its last token), through the block
-// table in 16-token tiles shared by the four waves: every lane loads one
-// 16-byte unit of a K row and of a V row into double-buffered LDS tiles (one
-// barrier per tile; the next tile's loads are in flight while the current one
-// is computed), and each wave reads its MFMA operands from there, masking the
-// tokens after its own columns' positions.  Sharing each tile between four
+// table in 32-token tiles shared by the four waves: per 16-token chunk, every
+// lane loads one 16-byte unit of a K row and of a V row into double-buffered
+// LDS tiles (one barrier per tile; the next tile's loads are in flight while
+// the current one is computed), and each wave reads its K and V operands
+// from there (its Q operands stay in registers), masking the tokens after its
+// own columns' positions on the tiles that reach them.  Sharing each tile between four
 // waves cuts the K/V reads per query four times against one wave per tile.
 // Items are numbered sequence by sequence from the per-sequence counts (a
 // prefix scan in LDS) and dispatched from the last to the first, so the
@@ -55,6 +56,37 @@ constexpr int kTileRows = 16 * kTC;      // tokens per tile
 static_assert(kItemThreads == 16 * 16, "one 16-byte unit of 16 rows per lane and chunk");
 
 constexpr int kXcds = 8;  // XCDs of the device; workgroups go round-robin over them
+
+#ifndef PKV_PREFILL_STALE_MAX
+#define PKV_PREFILL_STALE_MAX 8  // log2 headroom of the running max (0: move it with every tile max)
+#endif
+
+// Online-softmax step of one column that moves the running max m only when
+// the tile's maximum exceeds it by more than 2^PKV_PREFILL_STALE_MAX.  Until
+// then the probabilities exp2(x - m) stay below 2^PKV_PREFILL_STALE_MAX
+// (far from the fp32 range, and split into bf16 hi + lo as before) and the
+// accumulators need no rescaling.  The normalised result o / l does not
+// depend on the m it was accumulated with, so only rounding changes; with a
+// causal mask the running max of 32 query columns otherwise moves in most
+// tiles of a prompt.  Returns the factor that rescales the state so far
+// (exactly 1 when m stays).
+template <int TC>
+__device__ __forceinline__ float softmax_update_stale(float (&x)[TC][4], float mt, float& m,
+                                                      float& l) {
+  const float m_new = mt > m + float(PKV_PREFILL_STALE_MAX) ? mt : m;  // m = -inf: takes mt
+  const float alpha = exp2_hw(m - m_new);
+  m = m_new;
+  float psum = 0.f;
+#pragma unroll
+  for (int c = 0; c < TC; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[c][i] = exp2_hw(x[c][i] - m_new);
+      psum += x[c][i];
+    }
+  l = l * alpha + psum;
+  return alpha;
+}
 
 // Bijection of [0, n): workgroup id p (on XCD p % kXcds) -> a logical id such
 // that each XCD holds a contiguous range of logical ids.
@@ -91,7 +123,6 @@ __global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa
   __shared__ u32x4_t s_v[2][kTileRows * kVRowPad];
   __shared__ float s_ks[2][F8 ? kTileRows : 1];  // FP8 pools: K and V scale of each row's block
   __shared__ float s_vs[2][F8 ? kTileRows : 1];
-  __shared__ u32x4_t s_q[kItemWaves][kSharedSets][4][64];  // each lane's Q operands
   __shared__ int s_item[kMaxBalancedSeqs + 1];  // first work item of each sequence
   __shared__ int s_wsum[kItemWaves];
 
@@ -131,18 +162,15 @@ __global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa
   const int wt1 = min(t1, wt0 + QW);
 
   // Columns: query rows and causal limits (a column past the item's last
-  // token repeats it; its output is not stored).  The Q operands wait in LDS
-  // (read back for every tile), which leaves the registers to two tiles of
-  // loads in flight.
+  // token repeats it; its output is not stored).  The Q operands stay in
+  // registers for the whole key range.
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
   CausalTokens<kSharedSets> lim;
+  bf16x8_t qop[kSharedSets][4];
 #pragma unroll
   for (int s = 0; s < kSharedSets; ++s) {
     const int t = min(wt0 + (16 * s + col) / G, t1 - 1);
-    bf16x8_t qo[4];
-    load_qop(q + ((int64_t)(r0 + t) * a.num_q_heads + kvh * G + col % G) * kD, qr, qo);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) s_q[wave][s][k][lane] = __builtin_bit_cast(u32x4_t, qo[k]);
+    load_qop(q + ((int64_t)(r0 + t) * a.num_q_heads + kvh * G + col % G) * kD, qr, qop[s]);
     lim.limit[s] = pos0 + t + 1;
   }
   MfmaState<kSharedSets> st;
@@ -157,8 +185,12 @@ __global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa
   const uint8_t* vbase8 = static_cast<const uint8_t*>(a.v_cache) + (int64_t)kvh * kD + 8 * ucol;
   const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
   const int kend = pos0 + t1;  // key tokens of the item: 0 .. kend - 1
+  // Every column attends to the keys before its first column's limit.
+  const int first_limit = pos0 + min(wt0, t1 - 1) + 1;
   for (int w0 = 0; w0 < kend; w0 += kMaxPartitionTokens) {
     const int wend = min(kend, w0 + kMaxPartitionTokens);
+    // tiles that end at or before this key need no mask
+    const int mask_from = min(wend, first_limit);
     const int blk0 = w0 / BS;
     const int nblk = (wend - 1) / BS - blk0 + 1;
     __syncthreads();  // every wave is done with the previous window's ids and tiles
@@ -202,15 +234,8 @@ __global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa
       }
     };
     auto compute = [&](int buf, int tt) {
-      bf16x8_t qop[kSharedSets][4];
-#pragma unroll
-      for (int m = 0; m < kSharedSets; ++m)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) qop[m][k] = __builtin_bit_cast(bf16x8_t, s_q[wave][m][k][lane]);
       const u32x4_t* kt = s_k[buf];
       float x[kSharedSets][kTC][4], mt[kSharedSets], alpha[kSharedSets];
-#pragma unroll
-      for (int m = 0; m < kSharedSets; ++m) mt[m] = -INFINITY;
 #pragma unroll
       for (int c = 0; c < kTC; ++c) {
         u32x4_t kop[4];
@@ -219,12 +244,38 @@ __global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa
         // FP8: the lane's 4 rows (4 qr ..) lie in one block; its K scale
         // multiplies their scores
         const float sl = F8 ? a.scale_log2e * s_ks[buf][16 * c + 4 * qr] : a.scale_log2e;
-        scores_from_kop<kTC, kSharedSets>(kop, c, tt + 16 * c, wend, qop, sl, qr, x, mt, lim);
+#pragma unroll
+        for (int m = 0; m < kSharedSets; ++m) {
+          f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop[s]),
+                                                            qop[m][s], sacc, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[m][c][i] = sacc[i] * sl;
+        }
+      }
+      if (tt + kTileRows > mask_from) {  // the causal diagonal or the window's end
+#pragma unroll
+        for (int c = 0; c < kTC; ++c)
+#pragma unroll
+          for (int m = 0; m < kSharedSets; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (!lim.valid(m, tt + 16 * c + 4 * qr + i, wend)) x[m][c][i] = -INFINITY;
+      }
+#pragma unroll
+      for (int m = 0; m < kSharedSets; ++m) {
+        mt[m] = -INFINITY;
+#pragma unroll
+        for (int c = 0; c < kTC; ++c)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mt[m] = fmaxf(mt[m], x[m][c][i]);
       }
       column_max<kSharedSets>(mt);
 #pragma unroll
       for (int m = 0; m < kSharedSets; ++m)
-        alpha[m] = softmax_update<kTC>(x[m], mt[m], st.m[m], st.l[m]);
+        alpha[m] = softmax_update_stale<kTC>(x[m], mt[m], st.m[m], st.l[m]);
       if constexpr (F8) {  // dequantised V = scale * code: scale the probabilities (not l)
 #pragma unroll
         for (int c = 0; c < kTC; ++c) {

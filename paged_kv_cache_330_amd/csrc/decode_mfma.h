@@ -330,14 +330,29 @@ __device__ __forceinline__ void scores_from_kop(const u32x4_t (&kop)[4], int c, 
   }
 }
 
+// Maximum of x over lanes l and l ^ 16, then l ^ 32: the four row groups of
+// a column.  The gfx950 lane swaps exchange 16-lane rows (row 2k + 1 of the
+// first operand with row 2k of the second) and 32-lane halves without going
+// through LDS; the maximum of the two results is symmetric in the pair.
+__device__ __forceinline__ float rowgroup_max(float x) {
+#if PKV_PERMLANE_MAX
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t v = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+#else
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+#endif
+}
+
 // Column maxima over the four row groups of a wave.
 template <int NS>
 __device__ __forceinline__ void column_max(float (&mt)[NS]) {
 #pragma unroll
-  for (int n = 0; n < NS; ++n) {
-    mt[n] = fmaxf(mt[n], __shfl_xor(mt[n], 16));
-    mt[n] = fmaxf(mt[n], __shfl_xor(mt[n], 32));
-  }
+  for (int n = 0; n < NS; ++n) mt[n] = rowgroup_max(mt[n]);
 }
 
 // Q.K^T of one loaded tile for NS sets of query columns, scaled by

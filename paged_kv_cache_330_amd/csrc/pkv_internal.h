@@ -42,6 +42,9 @@ constexpr int kMaxBalancedSeqs = 2048;     // batch limit of the balanced schedu
 #ifndef PKV_PV_PAIRS
 #define PKV_PV_PAIRS 1          // several chunks per tile: P.V of chunk pairs with the 16x16x32 product
 #endif
+#ifndef PKV_PERMLANE_MAX
+#define PKV_PERMLANE_MAX 1      // column maxima across row groups with v_permlane{16,32}_swap (0: ds_bpermute)
+#endif
 #ifndef PKV_LAZY_RESCALE
 #define PKV_LAZY_RESCALE 1      // P.V accumulators rescaled only in tiles where a running max moved
 #endif
