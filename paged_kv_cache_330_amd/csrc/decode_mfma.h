@@ -64,15 +64,22 @@ constexpr int kMaxWaves = 8;
 #endif
 
 // Eight E4M3 codes widened to eight bf16 values, exactly (an E4M3 value has
-// at most 4 significant bits); gfx950's conversion decodes OCP E4M3.
+// at most 4 significant bits); gfx950's conversions decode OCP E4M3.  The
+// scaled conversion with scale 1 gives two bf16 per instruction; the other
+// path goes through fp32 and keeps the top halves.
 __device__ __forceinline__ u32x4_t widen_e4m3(u32x2_t w) {
   u32x4_t r;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
+#if PKV_FP8_SCALED_CVT
+    r[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[j], 1.f, false));
+    r[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[j], 1.f, true));
+#else
     const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], false);  // codes 4j, 4j + 1
     const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], true);   // codes 4j + 2, 4j + 3
     r[2 * j] = __builtin_amdgcn_perm(__float_as_uint(lo.y), __float_as_uint(lo.x), 0x07060302u);
     r[2 * j + 1] = __builtin_amdgcn_perm(__float_as_uint(hi.y), __float_as_uint(hi.x), 0x07060302u);
+#endif
   }
   return r;
 }

@@ -42,6 +42,9 @@ constexpr int kMaxBalancedSeqs = 2048;     // batch limit of the balanced schedu
 #ifndef PKV_PV_PAIRS
 #define PKV_PV_PAIRS 1          // several chunks per tile: P.V of chunk pairs with the 16x16x32 product
 #endif
+#ifndef PKV_FP8_SCALED_CVT
+#define PKV_FP8_SCALED_CVT 1    // E4M3 -> bf16 with v_cvt_scalef32_pk_bf16_fp8 (0: via fp32 and a byte permute)
+#endif
 #ifndef PKV_PERMLANE_MAX
 #define PKV_PERMLANE_MAX 1      // column maxima across row groups with v_permlane{16,32}_swap (0: ds_bpermute)
 #endif
