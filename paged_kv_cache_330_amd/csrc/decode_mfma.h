@@ -157,6 +157,11 @@ struct TileCtx {
   const float* kscale;    // FP8 pools: scales [num_blocks][num_kv_heads] + kv head
   const float* vscale;
   int scale_stride;       // FP8 pools: num_kv_heads
+  const uint8_t* kpool;   // K pool + kv head offset, in bytes (wave-uniform)
+  const uint8_t* vpool;   // V pool + kv head offset, in bytes (wave-uniform)
+  uint32_t row_bytes;     // bytes between consecutive slots
+  uint32_t lane_bytes;    // this lane's byte offset inside a row (dims 8 col ..)
+  uint32_t row_off[4];    // (4 qr + i) * row_bytes + lane_bytes: this lane's bytes of row i of a chunk
   u32x4_t* k_lds;         // this wave's K transpose tile (PKV_K_VIA_LDS)
   u32x4_t* v_lds;         // this wave's V tile, read column-wise (P.V on the matrix cores)
   int64_t tok_stride;     // elements between consecutive slots
@@ -218,6 +223,36 @@ __device__ __forceinline__ void load_tile(KVTile<TC, F8>& r, int t0, const TileC
     }
 #if PKV_K_VIA_LDS
     (void)pk;
+    if constexpr (BS >= 16 && PKV_SCALAR_BLOCK_BASE && (F8 || (TC == 1 && PKV_DEAD_REREAD))) {
+      // The chunk lies in one block: its first row's address is wave-uniform
+      // (scalar registers) and a lane adds only the 32-bit offset of its row,
+      // row 4 qr + i clamped to the window's last token, which is the same
+      // row as below (tce is a multiple of 16, so tce + r stays in the block).
+      // min(r, lim) * row_bytes = min(r * row_bytes, lim * row_bytes).
+      const int tcu = __builtin_amdgcn_readfirstlane(tce);
+      const int lim = __builtin_amdgcn_readfirstlane(c.end - 1 - tcu);  // >= 0: tce <= last_chunk
+      const int64_t first = ((int64_t)pk * BS + (tcu & (BS - 1))) * c.row_bytes;
+      const uint8_t* kb = c.kpool + first;
+      const uint8_t* vb = c.vpool + first;
+      const uint32_t lim_off = (uint32_t)lim * c.row_bytes + c.lane_bytes;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t off = min(c.row_off[i], lim_off);
+        if constexpr (F8) {
+          r.k[ch][i] = load_kv8(kb + off);
+          r.v[ch][i] = load_kv8(vb + off);
+        } else {
+          r.k[ch][i] = load_kv(reinterpret_cast<const uint16_t*>(kb + off));
+          r.v[ch][i] = load_kv(reinterpret_cast<const uint16_t*>(vb + off));
+        }
+      }
+      if constexpr (F8) {
+        const int64_t si = (int64_t)pk * c.scale_stride;
+        r.ks[ch] = c.kscale[si];
+        r.vs[ch] = c.vscale[si];
+      }
+      continue;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {  // row 4 qr + i, dims 8 col .. 8 col + 7
       const int tv = min(tce + 4 * c.qr + i, c.end - 1);
@@ -301,8 +336,11 @@ using WaveState = std::conditional_t<kPvOnMfma<G>, MfmaState<1>, ValuState<G>>;
 // Which tokens of a window a query column attends to.  WindowTokens: all of
 // them (decode).  CausalTokens: column set n of this lane stops below
 // limit[n] (prefill: a token sees the tokens up to its own position).
+// whole(tok0, end): every column attends to all 16 tokens from tok0 (a
+// wave-uniform test that lets the per-token test be skipped).
 struct WindowTokens {
   __device__ __forceinline__ bool valid(int, int tok, int end) const { return tok < end; }
+  __device__ __forceinline__ bool whole(int tok0, int end) const { return tok0 + 16 <= end; }
 };
 template <int NS>
 struct CausalTokens {
@@ -310,6 +348,7 @@ struct CausalTokens {
   __device__ __forceinline__ bool valid(int n, int tok, int end) const {
     return tok < end && tok < limit[n];
   }
+  __device__ __forceinline__ bool whole(int, int) const { return false; }
 };
 
 // Q.K^T of chunk c (tokens tok0 .. tok0 + 15) for NS sets of query columns
@@ -329,11 +368,14 @@ __device__ __forceinline__ void scores_from_kop(const u32x4_t (&kop)[4], int c, 
       sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop[s]),
                                                       qop[n][s], sacc, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tok = tok0 + 4 * qr + i;
-      x[n][c][i] = lim.valid(n, tok, end) ? sacc[i] * sl : -INFINITY;
-      mt[n] = fmaxf(mt[n], x[n][c][i]);
+    for (int i = 0; i < 4; ++i) x[n][c][i] = sacc[i] * sl;
+    if (!lim.whole(tok0, end)) {  // only a window's last chunk holds tokens past its end
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (!lim.valid(n, tok0 + 4 * qr + i, end)) x[n][c][i] = -INFINITY;
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mt[n] = fmaxf(mt[n], x[n][c][i]);
   }
 }
 
@@ -698,6 +740,15 @@ __device__ __forceinline__ void attend_table(const DecodeArgs& a, int* s_bt, u32
   c.vdead = qrow + 8 * c.col;
   c.v_lds = v_lds;
   c.s_bt = s_bt;
+  {
+    constexpr int es = F8 ? 1 : 2;  // bytes per stored element
+    c.kpool = static_cast<const uint8_t*>(a.k_cache) + (int64_t)kvh * kD * es;
+    c.vpool = static_cast<const uint8_t*>(a.v_cache) + (int64_t)kvh * kD * es;
+    c.row_bytes = (uint32_t)(c.tok_stride * es);
+    c.lane_bytes = (uint32_t)(8 * c.col * es);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c.row_off[i] = (uint32_t)(4 * c.qr + i) * c.row_bytes + c.lane_bytes;
+  }
   if constexpr (F8) {
     c.kbase8 = static_cast<const uint8_t*>(a.k_cache) + (int64_t)kvh * kD + 8 * c.col;
     c.vbase8 = static_cast<const uint8_t*>(a.v_cache) + (int64_t)kvh * kD + 8 * c.col;

@@ -54,6 +54,9 @@ constexpr int kMaxBalancedSeqs = 2048;     // batch limit of the balanced schedu
 #ifndef PKV_KV_NONTEMPORAL
 #define PKV_KV_NONTEMPORAL 1    // K/V loads carry the streaming hint (0: plain loads)
 #endif
+#ifndef PKV_SCALAR_BLOCK_BASE
+#define PKV_SCALAR_BLOCK_BASE 1 // block_size >= 16: a chunk's block address in scalar registers, 32-bit lane offsets
+#endif
 #ifndef PKV_K_VIA_LDS
 #define PKV_K_VIA_LDS 1         // K rows loaded 4 whole rows per instruction, transposed in LDS (0: MFMA layout loads)
 #endif
