@@ -44,6 +44,12 @@ namespace {
 #ifndef PKV_PREFILL_CHUNKS
 #define PKV_PREFILL_CHUNKS 2  // 16-token chunks per shared K/V tile
 #endif
+#ifndef PKV_PREFILL_SCALAR_BASE
+#define PKV_PREFILL_SCALAR_BASE 1  // block_size >= 16: chunk address in scalar registers, 32-bit lane offsets
+#endif
+#ifndef PKV_PREFILL_FOLD_SCALE
+#define PKV_PREFILL_FOLD_SCALE 1   // bf16: score factor applied in the exponent's fused multiply-add
+#endif
 #ifndef PKV_PREFILL_PV32
 #define PKV_PREFILL_PV32 1    // P.V of chunk pairs with the 16x16x32 product
 #endif
@@ -82,6 +88,29 @@ __device__ __forceinline__ float softmax_update_stale(float (&x)[TC][4], float m
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       x[c][i] = exp2_hw(x[c][i] - m_new);
+      psum += x[c][i];
+    }
+  l = l * alpha + psum;
+  return alpha;
+}
+
+// softmax_update_stale for raw scores x (not yet multiplied by the positive
+// factor sl = scale * log2(e)) and their raw tile maximum mt: since sl > 0,
+// the maximum of the scaled scores is mt * sl, and the scaled score enters
+// the exponent through one fused multiply-add, exp2(x * sl - m).
+template <int TC>
+__device__ __forceinline__ float softmax_update_stale_raw(float (&x)[TC][4], float mt, float sl,
+                                                          float& m, float& l) {
+  const float mts = mt * sl;
+  const float m_new = mts > m + float(PKV_PREFILL_STALE_MAX) ? mts : m;  // m = -inf: takes mts
+  const float alpha = exp2_hw(m - m_new);
+  m = m_new;
+  float psum = 0.f;
+#pragma unroll
+  for (int c = 0; c < TC; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[c][i] = exp2_hw(fmaf(x[c][i], sl, -m_new));
       psum += x[c][i];
     }
   l = l * alpha + psum;
@@ -173,6 +202,25 @@ __global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa
     load_qop(q + ((int64_t)(r0 + t) * a.num_q_heads + kvh * G + col % G) * kD, qr, qop[s]);
     lim.limit[s] = pos0 + t + 1;
   }
+  // bf16 pools: the score factor sl = scale * log2(e) is applied inside the
+  // exponent (softmax_update_stale_raw), which needs sl > 0.  A negative
+  // scale negates the query operands instead (exact: a sign flip of every
+  // bf16 value negates every product and sum), and sl = 0 is raised to the
+  // smallest normal float, which leaves every exponent's rounding unchanged
+  // (|score| * 2^-126 is far below half an ulp of the maximum's shift).
+  constexpr bool kFold = !F8 && PKV_PREFILL_FOLD_SCALE;
+  float slf = a.scale_log2e;
+  if constexpr (kFold) {
+    if (slf < 0.f) {
+#pragma unroll
+      for (int s = 0; s < kSharedSets; ++s)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          qop[s][k] = __builtin_bit_cast(bf16x8_t, __builtin_bit_cast(u32x4_t, qop[s][k]) ^ 0x80008000u);
+      slf = -slf;
+    }
+    slf = fmaxf(slf, 1.17549435e-38f);
+  }
   MfmaState<kSharedSets> st;
   st.reset();
 
@@ -183,6 +231,12 @@ __global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v_cache) + (int64_t)kvh * kD + 8 * ucol;
   const uint8_t* kbase8 = static_cast<const uint8_t*>(a.k_cache) + (int64_t)kvh * kD + 8 * ucol;
   const uint8_t* vbase8 = static_cast<const uint8_t*>(a.v_cache) + (int64_t)kvh * kD + 8 * ucol;
+  constexpr int es = F8 ? 1 : 2;  // bytes per stored element
+  const uint8_t* kpool = static_cast<const uint8_t*>(a.k_cache) + (int64_t)kvh * kD * es;
+  const uint8_t* vpool = static_cast<const uint8_t*>(a.v_cache) + (int64_t)kvh * kD * es;
+  const uint32_t row_bytes = (uint32_t)(tok_stride * es);
+  const uint32_t lane_bytes = (uint32_t)(8 * ucol * es);
+  const uint32_t row_off = (uint32_t)urow * row_bytes + lane_bytes;
   const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
   const int kend = pos0 + t1;  // key tokens of the item: 0 .. kend - 1
   // Every column attends to the keys before its first column's limit.
@@ -198,9 +252,31 @@ __global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa
       s_bt[i] = checked_block(bt, blk0 + i, a.num_blocks, a.err);
     __syncthreads();
     // Rows past the window's end re-read its last token (masked).
+    const int last_chunk = ((wend - 1) >> 4) << 4;  // start of the window's last 16-token chunk
     auto load_units = [&](int tt, TileUnits<F8>& u) {
 #pragma unroll
       for (int c = 0; c < kTC; ++c) {
+        if constexpr (BS >= 16 && PKV_PREFILL_SCALAR_BASE) {
+          // The chunk lies in one block: its address is wave-uniform and a
+          // lane adds the 32-bit offset of its row, clamped to the window's
+          // last token.  A chunk wholly past the end re-reads the last chunk
+          // (never computed unmasked).
+          const int tce = __builtin_amdgcn_readfirstlane(min(tt + 16 * c, last_chunk));
+          const int lim = __builtin_amdgcn_readfirstlane(wend - 1 - tce);  // >= 0
+          const int phys = __builtin_amdgcn_readfirstlane(s_bt[tce / BS - blk0]);
+          const int64_t first = ((int64_t)phys * BS + (tce & (BS - 1))) * row_bytes;
+          const uint32_t off = min(row_off, (uint32_t)lim * row_bytes + lane_bytes);
+          if constexpr (F8) {
+            u.k[c] = *reinterpret_cast<const u32x2_t*>(kpool + first + off);
+            u.v[c] = *reinterpret_cast<const u32x2_t*>(vpool + first + off);
+            u.ks[c] = a.k_scale[(int64_t)phys * a.num_kv_heads + kvh];
+            u.vs[c] = a.v_scale[(int64_t)phys * a.num_kv_heads + kvh];
+          } else {
+            u.k[c] = *reinterpret_cast<const u32x4_t*>(kpool + first + off);
+            u.v[c] = *reinterpret_cast<const u32x4_t*>(vpool + first + off);
+          }
+          continue;
+        }
         const int tok = min(tt + 16 * c + urow, wend - 1);
         const int phys = s_bt[tok / BS - blk0];
         const int64_t row = ((int64_t)phys * BS + (tok & (BS - 1))) * tok_stride;
@@ -252,7 +328,7 @@ __global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa
             sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop[s]),
                                                             qop[m][s], sacc, 0, 0, 0);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) x[m][c][i] = sacc[i] * sl;
+          for (int i = 0; i < 4; ++i) x[m][c][i] = kFold ? sacc[i] : sacc[i] * sl;
         }
       }
       if (tt + kTileRows > mask_from) {  // the causal diagonal or the window's end
@@ -275,7 +351,8 @@ __global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa
       column_max<kSharedSets>(mt);
 #pragma unroll
       for (int m = 0; m < kSharedSets; ++m)
-        alpha[m] = softmax_update_stale<kTC>(x[m], mt[m], st.m[m], st.l[m]);
+        alpha[m] = kFold ? softmax_update_stale_raw<kTC>(x[m], mt[m], slf, st.m[m], st.l[m])
+                         : softmax_update_stale<kTC>(x[m], mt[m], st.m[m], st.l[m]);
       if constexpr (F8) {  // dequantised V = scale * code: scale the probabilities (not l)
 #pragma unroll
         for (int c = 0; c < kTC; ++c) {

@@ -7,6 +7,7 @@ oracle.prefill_ref).
   chunk-edge lengths, chunks after cached context, every query group size and
   block size, sequences with no new token, a chunk across the 4096-token
   load window and a 4200-token prompt (sampled rows);
+* any finite scale, negative and zero included;
 * one new token per sequence gives the decode result;
 * inconsistent query ranges are flagged in the device error word.
 """
@@ -107,6 +108,22 @@ def test_prefill_matches_oracle(ops, case):
     assert np.array_equal(host_bits(vc).view(np.uint8), rv.view(np.uint8)), "V pool bytes differ"
     ref = oracle.prefill_ref(w.q, w.query_start, rk, rv, w.block_tables, w.seq_lens, w.scale, "bf16")
     assert_close(out.cpu().numpy(), ref, name)
+
+
+@pytest.mark.parametrize("scale", [-0.0883883, 0.0, 0.3, 1e-30])
+def test_prefill_any_scale(ops, scale):
+    """The kernel applies the score factor inside the exponent, which needs a
+    positive factor: a negative scale negates the queries instead, and zero
+    (uniform attention over each token's keys) is raised to the smallest
+    normal float.  Every such scale matches the oracle."""
+    say(f"case scale {scale}")
+    w = PrefillWorkload([20, 0, 5], [40, 33, 17], block_size=16, num_q_heads=32, num_kv_heads=8,
+                        seed=11)
+    w.scale = np.float32(scale)
+    kc, vc, out = run(ops, w)
+    rk, rv = oracle_pools(w)
+    ref = oracle.prefill_ref(w.q, w.query_start, rk, rv, w.block_tables, w.seq_lens, w.scale, "bf16")
+    assert_close(out.cpu().numpy(), ref, f"scale {scale}")
 
 
 @pytest.mark.parametrize("context,new", [([4090], [20]), ([0], [4200])],
