@@ -446,7 +446,11 @@ def sharing_step_state(torch, ops, ws, final, partition_tokens, shared=False, fp
 
 
 def time_steps(torch, step, steps, warmup):
-    """Warm up, then time exactly `steps` steps between two synchronisations.
+    """Warm up, then time exactly `steps` steps between two synchronisations;
+    then run the same `steps` steps again with stream events around each phase
+    for the per-phase times.  The wall time comes from the first pass, which
+    has no events between its launches (each event is a command of its own on
+    the stream).
 
     Re-running a step is idempotent: its copies, writes and decode see the same
     pool contents every time."""
@@ -454,13 +458,17 @@ def time_steps(torch, step, steps, warmup):
         step.run(i)
     torch.cuda.synchronize()
     step.ops.pkv_check_device_errors()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step.run(warmup + i, events[i])
+        step.run(warmup + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    step.ops.pkv_check_device_errors()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for i in range(steps):
+        step.run(warmup + steps + i, events[i])
+    torch.cuda.synchronize()
     step.ops.pkv_check_device_errors()
     ms = lambda a, b: [e[a].elapsed_time(e[b]) for e in events]  # noqa: E731
     return wall, ms(0, 1), ms(1, 2), ms(2, 3)
