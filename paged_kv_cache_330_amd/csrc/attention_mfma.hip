@@ -80,6 +80,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) PKV_BALANCED_OCCUPANCY void decode_
   __shared__ u32x4_t s_vt[kPvOnMfma<G> ? kMaxWaves * 16 * TC * kVRowPad : 1];
   __shared__ int s_cc[kMaxBalancedSeqs + 1];
   __shared__ int s_wsum[kMaxWaves];
+  __shared__ int s_prog[kMaxWaves];  // tiles streamed by each wave (issue balancing)
 
   const int nt = blockDim.x, nw = nt >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -88,6 +89,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) PKV_BALANCED_OCCUPANCY void decode_
   const int slice = blockIdx.y, S = gridDim.y;
   const int B = a.num_seqs;
   const bool reporter = blockIdx.x == 0 && slice == 0;
+  if (threadIdx.x < kMaxWaves) s_prog[threadIdx.x] = 0;  // visible after the scan's barriers
   // Merge descriptor of this slice: no split sequence ends here (yet).
   int* desc = a.ws_desc + 2 * slice;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -151,7 +153,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) PKV_BALANCED_OCCUPANCY void decode_
     st.reset();
     attend_range<G, BS, TC, F8>(a, s_bt, s_kt + (PKV_K_VIA_LDS ? wave * 16 * kKRowPad : 0),
                             s_vt + (kPvOnMfma<G> ? wave * 16 * TC * kVRowPad : 0), b, kvh, tok_begin,
-                            tok_end, qop, st);
+                            tok_end, qop, st, (PKV_WAVE_BALANCE && nw == 8) ? s_prog : nullptr);
     Sink sink{nullptr, nullptr, nullptr, 0, 0};
     if (!(first && last))
       sink = Sink{a.ws_acc, a.ws_max, a.ws_sum,

@@ -99,6 +99,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_shared_kernel(SharedArg
   __shared__ int s_cc[kMaxStreams + 1];         // first chunk of each stream
   __shared__ int s_wsum[kMaxWaves];
   __shared__ int s_bad;
+  __shared__ int s_prog[kMaxWaves];  // tiles streamed by each wave (issue balancing)
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -116,7 +117,9 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_shared_kernel(SharedArg
   //    <= B; otherwise the sharing is ignored.
   int NG = sa.num_groups;  // 0: the group arrays may be NULL and are not read
   if (threadIdx.x == 0) s_bad = 0;
+  if (threadIdx.x < kMaxWaves) s_prog[threadIdx.x] = 0;
   __syncthreads();
+  int* prog = (PKV_WAVE_BALANCE && blockDim.x == 8 * 64) ? s_prog : nullptr;
   for (int g = threadIdx.x; g <= NG && NG > 0; g += blockDim.x) {
     const int o = sa.group_offsets[g];
     s_goff[g] = o;
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_shared_kernel(SharedArg
                                  a.block_tables + (int64_t)lead * a.max_blocks_per_seq,
                                  q + ((int64_t)lead * a.num_q_heads + kvh * G) * kD, kvh,
                                  (c - cs) * 16, (c_end - cs) * 16, qop, ps,
-                                 TableCheck{sa.group_seqs + m0, nm});
+                                 TableCheck{sa.group_seqs + m0, nm}, WindowTokens{}, prog);
       store_columns(a, ps, ((int64_t)(st + slice) * a.num_kv_heads + kvh) * kCols, nm * G);
     } else {
       // Tail piece of sequence b: tokens T + 16 (c - cs) .. of its own table.
@@ -260,7 +263,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_shared_kernel(SharedArg
       WaveState<G> ws;
       ws.reset();
       attend_range<G, BS, TC, F8>(a, s_bt, k_lds, v_lds, b, kvh, T + (c - cs) * 16,
-                                  min(T + (c_end - cs) * 16, L), qop, ws);
+                                  min(T + (c_end - cs) * 16, L), qop, ws, prog);
       Sink sink{nullptr, nullptr, nullptr, 0, 0};
       if (!(T == 0 && c == cs && c_end == ce))
         sink = Sink{a.ws_acc, a.ws_max, a.ws_sum,

@@ -170,7 +170,22 @@ struct TileCtx {
   int end;                // one past the window's last token
   int last_chunk;         // start of the window's last 16-token chunk
   int col, qr;
+  volatile int* prog;     // LDS tile counts of the workgroup's waves (issue balancing), or nullptr
+  int wave;               // this wave's index in the workgroup
 };
+
+// Two waves share each SIMD (waves w and w + 4 of an 8-wave workgroup), and
+// the older one wins the issue arbitration: left alone it streams well ahead
+// of its partner, waits for it at the next barrier, and the workgroup's loads
+// in flight halve meanwhile.  Each wave counts its tiles in LDS and, when it
+// is behind its partner, raises its issue priority (and lowers it when ahead).
+__device__ __forceinline__ void balance_issue(const TileCtx& c) {
+  const int me = c.prog[c.wave] + 1;
+  c.prog[c.wave] = me;
+  const int other = c.prog[c.wave ^ 4];
+  if (me > other) __builtin_amdgcn_s_setprio(0);
+  else if (me < other) __builtin_amdgcn_s_setprio(2);
+}
 
 // 16 bytes of a K or V row; every K/V byte is read once per call, so the
 // loads may carry the streaming (non-temporal) hint.
@@ -689,6 +704,7 @@ __device__ __forceinline__ void stream_window(const DecodeArgs& a, const TileCtx
     __builtin_amdgcn_sched_barrier(0);
     compute_tile<TC>(tb, t0 + TILE, c.end, qop, a.scale_log2e, c, st, lim);
     t0 += 2 * TILE;
+    if (c.prog != nullptr) balance_issue(c);
   }
   if (n & 1) compute_tile<TC>(ta, t0, c.end, qop, a.scale_log2e, c, st, lim);
 #if PKV_DRAIN_PREFETCH
@@ -721,9 +737,11 @@ __device__ __forceinline__ void attend_table(const DecodeArgs& a, int* s_bt, u32
                                              const uint16_t* qrow, int kvh, int begin, int end,
                                              const bf16x8_t (&qop)[NS][4], State& st,
                                              TableCheck chk = TableCheck{nullptr, 0},
-                                             const Lim& lim = Lim{}) {
+                                             const Lim& lim = Lim{}, int* prog = nullptr) {
   const int lane = threadIdx.x & 63;
   TileCtx c;
+  c.prog = prog;
+  c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   c.tok_stride = (int64_t)a.num_kv_heads * kD;
   c.col = lane & 15;
   c.qr = lane >> 4;
@@ -785,11 +803,13 @@ __device__ __forceinline__ void attend_table(const DecodeArgs& a, int* s_bt, u32
 template <int G, int BS, int TC, bool F8 = false>
 __device__ __forceinline__ void attend_range(const DecodeArgs& a, int* s_bt, u32x4_t* k_lds,
                                              u32x4_t* v_lds, int b, int kvh, int begin, int end,
-                                             const bf16x8_t (&qop)[1][4], WaveState<G>& st) {
+                                             const bf16x8_t (&qop)[1][4], WaveState<G>& st,
+                                             int* prog = nullptr) {
   const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
   const uint16_t* qrow =
       static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.num_q_heads + kvh * G) * kD;
-  attend_table<BS, TC, false, F8>(a, s_bt, k_lds, v_lds, bt, qrow, kvh, begin, end, qop, st);
+  attend_table<BS, TC, false, F8>(a, s_bt, k_lds, v_lds, bt, qrow, kvh, begin, end, qop, st,
+                                  TableCheck{nullptr, 0}, WindowTokens{}, prog);
 }
 
 // Where a wave's finished range goes.

@@ -69,6 +69,9 @@ constexpr int kMaxBalancedSeqs = 2048;     // batch limit of the balanced schedu
 #ifndef PKV_BALANCED_MAX_WAVES
 #define PKV_BALANCED_MAX_WAVES 8 // most waves (kv heads) per workgroup of the balanced schedule
 #endif
+#ifndef PKV_WAVE_BALANCE
+#define PKV_WAVE_BALANCE 1 // balanced schedule: issue priority to the wave behind its SIMD partner
+#endif
 #ifndef PKV_BALANCED_WGS
 #define PKV_BALANCED_WGS 256    // workgroups of the balanced schedule (all kv-head groups)
 #endif
