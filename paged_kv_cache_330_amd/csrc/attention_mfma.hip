@@ -79,6 +79,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) PKV_BALANCED_OCCUPANCY void decode_
   __shared__ u32x4_t s_kt[PKV_K_VIA_LDS ? kMaxWaves * 16 * kKRowPad : 1];
   __shared__ u32x4_t s_vt[kPvOnMfma<G> ? kMaxWaves * 16 * TC * kVRowPad : 1];
   __shared__ int s_cc[kMaxBalancedSeqs + 1];
+  __shared__ int s_len[kMaxBalancedSeqs];  // clamped sequence lengths
   __shared__ int s_wsum[kMaxWaves];
   __shared__ int s_prog[kMaxWaves];  // tiles streamed by each wave (issue balancing)
 
@@ -101,7 +102,9 @@ __global__ __launch_bounds__(kMaxWaves * 64) PKV_BALANCED_OCCUPANCY void decode_
   int carry = 0;
   for (int base = 0; base < B; base += nt) {
     const int j = base + threadIdx.x;
-    const int cnt = j < B ? (clamped_len(a, BS, j, reporter) + 15) >> 4 : 0;
+    const int len = j < B ? clamped_len(a, BS, j, reporter) : 0;
+    if (j < B) s_len[j] = len;
+    const int cnt = (len + 15) >> 4;
     int x = cnt;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -142,7 +145,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) PKV_BALANCED_OCCUPANCY void decode_
     while (s_cc[b + 1] <= c) ++b;  // skip sequences with no chunks
     const int cb = s_cc[b], ce = s_cc[b + 1];
     const int c_end = min(c_hi, ce);
-    const int L = clamped_len(a, BS, b, false);
+    const int L = s_len[b];  // written before the scan's barriers
     const int tok_begin = (c - cb) * 16;
     const int tok_end = min((c_end - cb) * 16, L);
     const bool first = c == cb, last = c_end == ce;
