@@ -172,10 +172,14 @@ __global__ __launch_bounds__(kMaxWaves * 64) PKV_BALANCED_OCCUPANCY void decode_
 }
 
 // Merges the pieces of the sequence whose final piece lies in slice
-// blockIdx.x (if any): workgroup (slice, kv-head group), wave w for kv head
-// kvg * KH + w, lane for output dims 2 lane and 2 lane + 1.  The pieces are
-// merged with a running maximum, so the loads of all pieces are independent
-// and issued together: out = sum_p e^(m_p - M) acc_p / sum_p e^(m_p - M) l_p.
+// blockIdx.x (if any): workgroup (slice, kv-head group, query head g of the
+// group), wave w for kv head kvg * KH + w, lane for output dims 2 lane and
+// 2 lane + 1.  The pieces are merged with a running maximum,
+// out = sum_p e^(m_p - M) acc_p / sum_p e^(m_p - M) l_p (the loop is
+// unrolled, so the loads of several pieces are in flight together).  One
+// workgroup per query head keeps a long sequence's merge (one piece per
+// slice it spans, e.g. 32 pieces for 32768 tokens over 256 slices) from
+// resting on a single workgroup per kv-head group.
 template <int G>
 __global__ __launch_bounds__(kMaxWaves * 64) void balanced_reduce_kernel(DecodeArgs a) {
   const int slice = blockIdx.x;
@@ -183,38 +187,27 @@ __global__ __launch_bounds__(kMaxWaves * 64) void balanced_reduce_kernel(DecodeA
   if (b < 0) return;
   const int s0 = a.ws_desc[2 * slice + 1], s1 = slice;
   const int kvh = blockIdx.y * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int g = blockIdx.z;
   const int d = 2 * (threadIdx.x & 63);
   const float* __restrict__ wmax = a.ws_max;
   const float* __restrict__ wsum = a.ws_sum;
   const float* __restrict__ wacc = a.ws_acc;
-  float M[G], den[G], num0[G], num1[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    M[g] = -INFINITY;
-    den[g] = num0[g] = num1[g] = 0.f;
-  }
-  // All loads first (no store in between), merged with a running maximum.
-#pragma unroll 2
+  float M = -INFINITY, den = 0.f, num0 = 0.f, num1 = 0.f;
+#pragma unroll 8
   for (int s = s0; s <= s1; ++s) {
-    const int64_t r0 = ((int64_t)(s * a.num_kv_heads + kvh) * 2 + (s == s0 ? 1 : 0)) * G;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float m = wmax[r0 + g], l = wsum[r0 + g];
-      const float2 acc = *reinterpret_cast<const float2*>(wacc + (r0 + g) * kD + d);
-      const float Mn = fmaxf(M[g], m);
-      const float c_old = rescale(M[g], Mn), c_new = exp2_hw(m - Mn);
-      den[g] = den[g] * c_old + l * c_new;
-      num0[g] = num0[g] * c_old + acc.x * c_new;
-      num1[g] = num1[g] * c_old + acc.y * c_new;
-      M[g] = Mn;
-    }
+    const int64_t r = ((int64_t)(s * a.num_kv_heads + kvh) * 2 + (s == s0 ? 1 : 0)) * G + g;
+    const float m = wmax[r], l = wsum[r];
+    const float2 acc = *reinterpret_cast<const float2*>(wacc + r * kD + d);
+    const float Mn = fmaxf(M, m);
+    const float c_old = rescale(M, Mn), c_new = exp2_hw(m - Mn);
+    den = den * c_old + l * c_new;
+    num0 = num0 * c_old + acc.x * c_new;
+    num1 = num1 * c_old + acc.y * c_new;
+    M = Mn;
   }
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const int64_t o = ((int64_t)b * a.num_q_heads + kvh * G + g) * kD + d;
-    store_out(a, o, num0[g] / den[g]);
-    store_out(a, o + 1, num1[g] / den[g]);
-  }
+  const int64_t o = ((int64_t)b * a.num_q_heads + kvh * G + g) * kD + d;
+  store_out(a, o, num0 / den);
+  store_out(a, o + 1, num1 / den);
 }
 
 template <int G, bool F8>
@@ -246,7 +239,7 @@ hipError_t launch_balanced_g(const DecodeArgs& a, int block_size, int kh, hipStr
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  balanced_reduce_kernel<G><<<dim3(a.slices, a.num_kv_heads / kh), block, 0, s>>>(a);
+  balanced_reduce_kernel<G><<<dim3(a.slices, a.num_kv_heads / kh, G), block, 0, s>>>(a);
   return hipGetLastError();
 }
 
