@@ -172,7 +172,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) PKV_BALANCED_OCCUPANCY void decode_
 }
 
 // Merges the pieces of the sequence whose final piece lies in slice
-// blockIdx.x (if any): workgroup (slice, kv-head group, query head g of the
+// blockIdx.x (if any; with fewer sequences than slices, in the blockIdx.x-th
+// slice that names one): workgroup (slice, kv-head group, query head g of the
 // group), wave w for kv head kvg * KH + w, lane for output dims 2 lane and
 // 2 lane + 1.  The pieces are merged with a running maximum,
 // out = sum_p e^(m_p - M) acc_p / sum_p e^(m_p - M) l_p (the loop is
@@ -182,7 +183,36 @@ __global__ __launch_bounds__(kMaxWaves * 64) PKV_BALANCED_OCCUPANCY void decode_
 // resting on a single workgroup per kv-head group.
 template <int G>
 __global__ __launch_bounds__(kMaxWaves * 64) void balanced_reduce_kernel(DecodeArgs a) {
-  const int slice = blockIdx.x;
+  int slice = blockIdx.x;
+  if (gridDim.x < a.slices) {
+    // Fewer workgroups than slices (there are fewer sequences than slices,
+    // and each cut sequence names one slice): workgroup r takes the r-th
+    // slice whose descriptor names a sequence, found by a ballot scan of all
+    // descriptors, so that no workgroup is launched idle for the rest.
+    __shared__ int s_cnt[kMaxWaves];
+    __shared__ int s_pick;
+    const int nw = blockDim.x >> 6, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (threadIdx.x == 0) s_pick = -1;
+    int before = 0;
+    for (int base = 0; base < a.slices; base += blockDim.x) {
+      const int t = base + threadIdx.x;
+      const bool named = t < a.slices && a.ws_desc[2 * t] >= 0;
+      const unsigned long long m = __ballot(named);
+      if (lane == 0) s_cnt[w] = __popcll(m);
+      __syncthreads();
+      int rank = before + __popcll(m & ((1ull << lane) - 1));
+      int total = 0;
+      for (int k = 0; k < nw; ++k) {
+        if (k < w) rank += s_cnt[k];
+        total += s_cnt[k];
+      }
+      if (named && rank == static_cast<int>(blockIdx.x)) s_pick = t;
+      before += total;
+      __syncthreads();  // s_cnt is rewritten by the next round; s_pick is final after the last
+    }
+    slice = s_pick;
+    if (slice < 0) return;
+  }
   const int b = a.ws_desc[2 * slice];
   if (b < 0) return;
   const int s0 = a.ws_desc[2 * slice + 1], s1 = slice;
@@ -239,7 +269,9 @@ hipError_t launch_balanced_g(const DecodeArgs& a, int block_size, int kh, hipStr
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  balanced_reduce_kernel<G><<<dim3(a.slices, a.num_kv_heads / kh, G), block, 0, s>>>(a);
+  // At most one slice per sequence names a cut sequence to merge.
+  const int reduce_wgs = a.num_seqs < a.slices ? a.num_seqs : a.slices;
+  balanced_reduce_kernel<G><<<dim3(reduce_wgs, a.num_kv_heads / kh, G), block, 0, s>>>(a);
   return hipGetLastError();
 }
 
