@@ -50,6 +50,9 @@ namespace {
 #ifndef PKV_PREFILL_FOLD_SCALE
 #define PKV_PREFILL_FOLD_SCALE 1   // bf16: score factor applied in the exponent's fused multiply-add
 #endif
+#ifndef PKV_PREFILL_MFMA_PRIO
+#define PKV_PREFILL_MFMA_PRIO 1  // issue priority 1 while a wave issues its matrix products
+#endif
 #ifndef PKV_PREFILL_PV32
 #define PKV_PREFILL_PV32 1    // P.V of chunk pairs with the 16x16x32 product
 #endif
@@ -312,6 +315,9 @@ __global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa
     auto compute = [&](int buf, int tt) {
       const u32x4_t* kt = s_k[buf];
       float x[kSharedSets][kTC][4], mt[kSharedSets], alpha[kSharedSets];
+#if PKV_PREFILL_MFMA_PRIO
+      __builtin_amdgcn_s_setprio(1);  // Q.K^T: this wave's products go first
+#endif
 #pragma unroll
       for (int c = 0; c < kTC; ++c) {
         u32x4_t kop[4];
@@ -331,6 +337,9 @@ __global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa
           for (int i = 0; i < 4; ++i) x[m][c][i] = kFold ? sacc[i] : sacc[i] * sl;
         }
       }
+#if PKV_PREFILL_MFMA_PRIO
+      __builtin_amdgcn_s_setprio(0);  // softmax: the other wave's products may go first
+#endif
       if (tt + kTileRows > mask_from) {  // the causal diagonal or the window's end
 #pragma unroll
         for (int c = 0; c < kTC; ++c)
@@ -364,6 +373,9 @@ __global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa
         }
       }
       rescale_lazy<kSharedSets>(alpha, st);
+#if PKV_PREFILL_MFMA_PRIO
+      __builtin_amdgcn_s_setprio(1);  // P.V
+#endif
       const uint16_t* vt = reinterpret_cast<const uint16_t*>(s_v[buf]);
 #if PKV_PREFILL_PV32
 #pragma unroll
@@ -378,6 +390,9 @@ __global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa
 #pragma unroll
       for (int c = 0; c < kTC; ++c)
         pv_from_lds<kTC, kSharedSets>(vt + 16 * c * kVRowPad * 8, c, x, col, qr, st);
+#endif
+#if PKV_PREFILL_MFMA_PRIO
+      __builtin_amdgcn_s_setprio(0);
 #endif
     };
     // Two tiles in flight: registers a and b alternate, tile t is computed
