@@ -152,6 +152,29 @@ def test_balanced_schedule_edges(ops, case):
     assert_close(out.cpu().numpy()[rows], oracle_decode(w, rk, rv, rows), TOL["bf16"], name)
 
 
+def test_balanced_reduce_over_named_slices(ops):
+    # Fewer sequences than slices with most of them cut: the reduce launches
+    # one workgroup per sequence and workgroup r merges the sequence named by
+    # the r-th slice that names one (ranks up to ~150 here), with empty
+    # sequences in between.  Every row is checked.
+    lens = (700, 0, 650, 730) * 50
+    w = workload(3, tuple(max(1, L) for L in lens), 16, None)
+    say(f"reduce over named slices: {len(lens)} sequences, {int(w.seq_lens.sum())} tokens")
+    kc, vc, _ = gpu_step(ops, w, decode=False)
+    sl = np.array(lens, np.int32)
+    out = torch.full((len(lens), w.num_q_heads, w.head_dim), 7.0, dtype=torch.float32, device="cuda")
+    ops.pkv_attention_decode(out, torch_tensor(w.q, "bf16", "cuda"), kc, vc,
+                             torch.from_numpy(w.block_tables).cuda(), torch.from_numpy(sl).cuda(),
+                             float(w.scale))
+    ops.pkv_check_device_errors()
+    rk, rv = oracle_caches(w)
+    got = out.cpu().numpy()
+    live = [i for i, L in enumerate(lens) if L > 0]
+    ref = oracle.decode_ref(w.q[live], rk, rv, w.block_tables[live], sl[live], w.scale, "bf16")
+    assert_close(got[live], ref, TOL["bf16"], "named slices")
+    assert (got[[i for i, L in enumerate(lens) if L == 0]] == 0).all()
+
+
 def test_balanced_schedule_zero_lengths_and_large_batch(ops):
     # zero-length rows inside a balanced batch, and a batch above the balanced
     # limit (2048 sequences) that falls back to the partition grid
