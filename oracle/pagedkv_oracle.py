@@ -271,19 +271,26 @@ def write_fp8_ref(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale) -> Non
     token whose slot lies in block ``blk`` becomes
     ``e4m3_encode(fp32(x / scale[blk, h]))``: the quotient is the binary32
     division of the two binary32 values, the same decision the device takes.
-    Negative slots are skipped, as by ``write_ref``.
+    Negative slots are skipped, as by ``write_ref``.  Tokens are taken in
+    order, a run of them at a time: inside a run every token's codes are formed
+    at once and a slot named twice keeps its later token, so the result is
+    that of writing the tokens one after another.
     """
     bs = k_cache.shape[1]
-    kx = widen(k, "bf16").astype(np.float32)
-    vx = widen(v, "bf16").astype(np.float32)
     ks = np.asarray(k_scale, dtype=np.float32)
     vs = np.asarray(v_scale, dtype=np.float32)
-    for i, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64).tolist()):
-        if slot < 0:
-            continue
-        blk, off = slot // bs, slot % bs
-        k_cache[blk, off] = e4m3_encode((kx[i] / ks[blk][:, None]).astype(np.float64))
-        v_cache[blk, off] = e4m3_encode((vx[i] / vs[blk][:, None]).astype(np.float64))
+    slots = np.asarray(slot_mapping, dtype=np.int64).reshape(-1)
+    run = 4096
+    for r0 in range(0, slots.size, run):
+        part = slots[r0:r0 + run]
+        rows = np.nonzero(part >= 0)[0]
+        # the last occurrence of each slot in the run: the first in reverse
+        _, first_rev = np.unique(part[rows][::-1], return_index=True)
+        rows = np.sort(rows[::-1][first_rev])
+        blk, off = part[rows] // bs, part[rows] % bs
+        for src, cache, sc in ((k, k_cache, ks), (v, v_cache, vs)):
+            x = widen(np.asarray(src)[r0 + rows], "bf16").astype(np.float32)   # [n, Hkv, D]
+            cache[blk, off] = e4m3_encode((x / sc[blk][:, :, None]).astype(np.float64))
 
 
 def dequantize_fp8(cache, scale) -> np.ndarray:

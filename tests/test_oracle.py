@@ -686,3 +686,45 @@ def test_write_fp8_ref_by_hand():
     deq = oracle.dequantize_fp8(kc, ks)
     assert deq[1, 1, 0].tolist() == [1.0, -3.0]
     oracle.write_fp8_ref(k, v, [-1], kc, vc, ks, vs)     # skipped
+
+
+def test_write_fp8_ref_many_tokens_round_trip_with_their_block_scales():
+    # Tokens whose values are exactly a grid value times their own block's
+    # (power-of-two) scale for that head come back exactly after dequantizing;
+    # every (block, head) has a different K and V scale, so taking the scale of
+    # another block, head or of the other pool breaks the round trip.  Runs of
+    # more than one token are formed at once: 10,000 tokens span three runs.
+    rng = np.random.default_rng(12)
+    NB, bs, hkv, d, n = 700, 16, 3, 8, 10_000
+    ks = np.exp2(rng.permutation(NB * hkv).reshape(NB, hkv) % 13 - 6).astype(np.float32)
+    vs = np.exp2(rng.permutation(NB * hkv).reshape(NB, hkv) % 11 - 5).astype(np.float32)
+    slots = rng.permutation(NB * bs)[:n].astype(np.int64)
+    grid = oracle.e4m3_value(np.arange(0x7F))[1:]                 # positive finite values
+    gk = rng.choice(grid, size=(n, hkv, d)) * rng.choice([-1.0, 1.0], size=(n, hkv, d))
+    gv = rng.choice(grid, size=(n, hkv, d)) * rng.choice([-1.0, 1.0], size=(n, hkv, d))
+    blk = slots // bs
+    xk = gk * ks[blk][:, :, None]
+    xv = gv * vs[blk][:, :, None]
+    k, v = bf16_round(xk.astype(np.float32)), bf16_round(xv.astype(np.float32))
+    assert np.array_equal(oracle.widen(k, "bf16"), xk) and np.array_equal(oracle.widen(v, "bf16"), xv)
+    kc = np.full((NB, bs, hkv, d), 0x7F, np.uint8)
+    vc = kc.copy()
+    oracle.write_fp8_ref(k, v, slots, kc, vc, ks, vs)
+    off = slots % bs
+    assert np.array_equal(oracle.dequantize_fp8(kc, ks)[blk, off], xk)
+    assert np.array_equal(oracle.dequantize_fp8(vc, vs)[blk, off], xv)
+    untouched = np.ones(NB * bs, bool)
+    untouched[slots] = False
+    assert (kc.reshape(NB * bs, hkv, d)[untouched] == 0x7F).all()
+
+
+def test_write_fp8_ref_later_token_wins_a_repeated_slot():
+    # a slot named twice in one call ends with the later token's codes, as for
+    # write_ref (a write in token order)
+    ks = np.ones((2, 1), np.float32)
+    k = bf16_round(np.array([[[1.0, 2.0]], [[4.0, 8.0]], [[0.5, 0.25]]], np.float32))
+    for slots, want in (([1, 1, -1], [4.0, 8.0]), ([1, 2, 1], [0.5, 0.25])):
+        kc = np.zeros((2, 2, 1, 2), np.uint8)
+        vc = kc.copy()
+        oracle.write_fp8_ref(k, k, slots, kc, vc, ks, ks)
+        assert oracle.dequantize_fp8(kc, ks)[0, 1, 0].tolist() == want
