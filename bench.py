@@ -52,9 +52,13 @@ def parse():
     p.add_argument("--prefix", type=int, default=2044, help="prefix-sharing workload: prompt tokens")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate budget of the CPU oracle sample")
+    p.add_argument("--report-cpu-seconds", type=float, default=4.0,
+                   help="approximate budget of the CPU oracle sample of each --report-all line")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--report-all", action="store_true",
-                   help="one line per workload (config 2, 4 at bs 32/64, 5 at bs 8/16), then the metric line")
+                   help="one line per workload (config 2, 4 at bs 32/64 with the balanced schedule "
+                        "and with 512-token partitions, 5 at bs 8/16, FP8, prefill), then the "
+                        "metric line")
     p.add_argument("--read-probe", action="store_true",
                    help="only time a plain streaming read of 4 GiB (context for the roofline)")
     p.add_argument("--copy-probe", action="store_true",
@@ -206,69 +210,222 @@ def measured_traffic():
     return int(val.group(1))
 
 
-def cpu_baseline(w, budget_s):
-    """The fp64 oracle on a bounded sample of the same workload.
+# The GPU machines give one GPU a share of 16 host cores (more may be visible):
+# the oracle's thread pool takes the cores this process may run on, at most 16.
+ORACLE_MAX_THREADS = 16
 
-    A pass is ``write_ref`` of the step's new tokens followed by ``decode_ref``
-    of a prefix of the batch (sequences 0..n-1), parallel over sequences.  The
-    prefix is sized from a one-sequence calibration to about ``budget_s``
-    seconds; when the whole batch takes less, whole passes repeat until the
-    budget is spent.
-    """
+
+def _oracle_threads():
+    cores = len(os.sched_getaffinity(0))
+    return max(1, min(ORACLE_MAX_THREADS, cores)), cores
+
+
+def _time_oracle(units, weights, one, budget_s, per_pass=None):
+    """Times the fp64 oracle on a bounded sample.
+
+    ``one(u)`` runs the oracle on work unit ``u`` (a sequence, a query row);
+    ``weights`` are the units' relative costs (tokens).  A one-unit
+    calibration sizes the sample: the first ``n`` units that fill about
+    ``budget_s`` seconds on the thread pool; when all units take less, whole
+    passes repeat until the budget is spent.  ``per_pass(units)`` runs first
+    in every pass (the step's writes and copies).  Returns
+    (n, passes, seconds, threads, visible cores)."""
     import numpy as np
     from concurrent.futures import ThreadPoolExecutor
     try:
         from threadpoolctl import threadpool_limits
     except Exception:  # pragma: no cover
         threadpool_limits = None
+    threads, cores = _oracle_threads()
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        t0 = time.perf_counter()
+        one(units[0])
+        per_w = (time.perf_counter() - t0) / max(1, int(weights[0]))
+        cum = np.cumsum(np.asarray(weights, dtype=np.int64))
+        target = budget_s * threads / max(per_w, 1e-9)
+        n = int(min(len(units), max(threads, np.searchsorted(cum, target) + 1)))
+        sample = units[:n]
+        passes = 0
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            while True:
+                if per_pass is not None:
+                    per_pass(sample)
+                list(ex.map(one, sample))
+                passes += 1
+                dt = time.perf_counter() - t0
+                if dt >= budget_s or n < len(units):
+                    break
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    return n, passes, dt, threads, cores
+
+
+def _baseline_entry(value, unit, n, passes, dt, threads, cores, sample, **extra):
+    return {"value": value, "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 3), "host_cpus_visible": cores,
+            "thread_cap": ORACLE_MAX_THREADS, **extra}
+
+
+def cpu_baseline(w, budget_s):
+    """The fp64 oracle on a bounded sample of decode workload ``w``.
+
+    A pass is ``write_ref`` of the step's new tokens of sequences 0..n-1
+    followed by ``decode_ref`` of those sequences (one call per sequence on
+    the thread pool); KV GB/s counts the K/V bytes the sample's attention
+    reads, as the GPU figure does."""
     import oracle
 
     kc, vc = w.empty_caches("zero")
     t0 = time.perf_counter()
     oracle.write_ref(w.k_tokens[w.prefill_rows], w.v_tokens[w.prefill_rows], w.prefill_slots, kc, vc)
     prefill_s = time.perf_counter() - t0
-    workers = max(1, min(16, len(os.sched_getaffinity(0))))
 
-    def run(r):
-        return oracle.decode_ref(w.q[[r]], kc, vc, w.block_tables[[r]], w.seq_lens[[r]],
-                                 w.scale, w.dtype)
+    def one(r):
+        return oracle.decode_ref(w.q[r:r + 1], kc, vc, w.block_tables[r:r + 1],
+                                 w.seq_lens[r:r + 1], w.scale, w.dtype)
 
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    if ctx:
-        ctx.__enter__()
-    try:
-        t0 = time.perf_counter()
-        run(0)
-        per_token = (time.perf_counter() - t0) / max(1, int(w.seq_lens[0]))
-        target_tokens = budget_s * workers / max(per_token, 1e-9)
-        cum = np.cumsum(w.seq_lens.astype(np.int64))
-        n = int(min(w.num_seqs, max(workers, np.searchsorted(cum, target_tokens) + 1)))
-        rows = list(range(n))
-        passes = 0
-        t0 = time.perf_counter()
-        with ThreadPoolExecutor(max_workers=workers) as ex:
-            while True:
-                oracle.write_ref(w.k_tokens[w.step_rows[rows]], w.v_tokens[w.step_rows[rows]],
-                                 w.step_slots[rows], kc, vc)
-                list(ex.map(run, rows))
-                passes += 1
-                dt = time.perf_counter() - t0
-                if dt >= budget_s or n < w.num_seqs:
-                    break
-    finally:
-        if ctx:
-            ctx.__exit__(None, None, None)
-    tokens = int(w.seq_lens[rows].sum())
+    def per_pass(rows):
+        oracle.write_ref(w.k_tokens[w.step_rows[rows]], w.v_tokens[w.step_rows[rows]],
+                         w.step_slots[rows], kc, vc)
+
+    n, passes, dt, threads, cores = _time_oracle(list(range(w.num_seqs)), w.seq_lens, one,
+                                                 budget_s, per_pass)
+    tokens = int(w.seq_lens[:n].sum())
     kv = passes * tokens * w.num_kv_heads * w.head_dim * 2 * w.elem_bytes
-    return {
-        "value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": workers, "kind": "oracle",
-        "sample": (f"{passes} pass(es) of write_ref of {n} new tokens + decode_ref of sequences "
-                   f"0..{n - 1} ({tokens} of {int(w.seq_lens.sum())} cached tokens) of the same "
-                   f"workload, fp64 NumPy, {workers} threads, {dt:.1f} s (prefill write_ref of "
-                   f"the pool, untimed: {prefill_s:.1f} s)"),
-        "seconds": round(dt, 3),
-        "tokens_per_s": round(passes * n / dt, 3),
-    }
+    return _baseline_entry(
+        round(kv / dt / 1e9, 4), "GB/s", n, passes, dt, threads, cores,
+        (f"{passes} pass(es) of write_ref of {n} new tokens + decode_ref of sequences "
+         f"0..{n - 1} ({tokens} of {int(w.seq_lens.sum())} cached tokens) of the same "
+         f"workload, fp64 NumPy, {threads} threads, {dt:.1f} s (prefill write_ref of "
+         f"the pool, untimed: {prefill_s:.1f} s)"),
+        tokens_per_s=round(passes * n / dt, 3))
+
+
+def cpu_baseline_fp8(w, ks, vs, budget_s):
+    """The fp64 oracle on a bounded sample of decode workload ``w`` over FP8
+    pools: a pass is ``write_fp8_ref`` of the new tokens of sequences 0..n-1,
+    then per sequence ``dequantize_fp8`` of its blocks and ``decode_ref``.
+    KV GB/s counts 1 byte per cached element, as the GPU figure does."""
+    import numpy as np
+    import oracle
+
+    shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
+    kc, vc = np.zeros(shape, np.uint8), np.zeros(shape, np.uint8)
+    t0 = time.perf_counter()
+    oracle.write_fp8_ref(w.k_tokens[w.prefill_rows], w.v_tokens[w.prefill_rows], w.prefill_slots,
+                         kc, vc, ks, vs)
+    prefill_s = time.perf_counter() - t0
+    q = oracle.widen(w.q, "bf16")
+
+    def one(r):
+        L = int(w.seq_lens[r])
+        nblk = -(-L // w.block_size)
+        blocks = w.block_tables[r, :nblk].astype(np.int64)
+        kd = oracle.dequantize_fp8(kc[blocks], ks[blocks])
+        vd = oracle.dequantize_fp8(vc[blocks], vs[blocks])
+        return oracle.decode_ref(q[r:r + 1], kd, vd, np.arange(nblk, dtype=np.int32)[None],
+                                 w.seq_lens[r:r + 1], w.scale, "f64")
+
+    def per_pass(rows):
+        oracle.write_fp8_ref(w.k_tokens[w.step_rows[rows]], w.v_tokens[w.step_rows[rows]],
+                             w.step_slots[rows], kc, vc, ks, vs)
+
+    n, passes, dt, threads, cores = _time_oracle(list(range(w.num_seqs)), w.seq_lens, one,
+                                                 budget_s, per_pass)
+    tokens = int(w.seq_lens[:n].sum())
+    kv = passes * tokens * w.num_kv_heads * w.head_dim * 2
+    return _baseline_entry(
+        round(kv / dt / 1e9, 4), "GB/s", n, passes, dt, threads, cores,
+        (f"{passes} pass(es) of write_fp8_ref of {n} new tokens + dequantize_fp8 and "
+         f"decode_ref of sequences 0..{n - 1} ({tokens} of {int(w.seq_lens.sum())} cached "
+         f"tokens), fp64 NumPy, {threads} threads, {dt:.1f} s (prefill write_fp8_ref of the "
+         f"pool, untimed: {prefill_s:.1f} s)"),
+        tokens_per_s=round(passes * n / dt, 3))
+
+
+def cpu_baseline_sharing(prefix, bs, prompts, final, budget_s):
+    """The fp64 oracle on the prefix-sharing workload at its first divergent
+    step or its last: the pool is built by the oracle's own writes and copies
+    of every earlier step (untimed); a pass is the step's ``copy_ref`` and
+    ``write_ref`` and ``decode_ref`` of sequences 0..n-1.  The oracle has one
+    definition of attention: the same pass serves the plain and the
+    shared-prefix decode.  KV GB/s counts the logical bytes every sequence
+    reads."""
+    import oracle
+    from paged_kv_cache_330_amd.workloads import PrefixSharingWorkload
+
+    ws = PrefixSharingWorkload(prefix_len=prefix, block_size=bs, prompts=prompts)
+    kc, vc = ws.empty_caches("zero")
+    t0 = time.perf_counter()
+    pk, pv, ps = ws.prefill()
+    oracle.write_ref(pk, pv, ps, kc, vc)
+    st = ws.next_step()
+    while final and ws.steps_done < ws.tail_len:
+        oracle.copy_ref(kc, vc, st.copy_pairs)
+        oracle.write_ref(st.k_new, st.v_new, st.slot_mapping, kc, vc)
+        st = ws.next_step()
+    build_s = time.perf_counter() - t0
+
+    def one(r):
+        return oracle.decode_ref(st.q[r:r + 1], kc, vc, st.block_tables[r:r + 1],
+                                 st.seq_lens[r:r + 1], ws.scale, "bf16")
+
+    def per_pass(rows):
+        oracle.copy_ref(kc, vc, st.copy_pairs)
+        oracle.write_ref(st.k_new[rows], st.v_new[rows], st.slot_mapping[rows], kc, vc)
+
+    n, passes, dt, threads, cores = _time_oracle(list(range(ws.num_seqs)), st.seq_lens, one,
+                                                 budget_s, per_pass)
+    tokens = int(st.seq_lens[:n].sum())
+    kv = passes * tokens * ws.num_kv_heads * ws.head_dim * 2 * 2
+    return _baseline_entry(
+        round(kv / dt / 1e9, 4), "GB/s", n, passes, dt, threads, cores,
+        (f"{passes} pass(es) of copy_ref of {len(st.copy_pairs)} pairs + write_ref of {n} new "
+         f"tokens + decode_ref of sequences 0..{n - 1} ({tokens} logical tokens) at step "
+         f"{ws.steps_done}, fp64 NumPy, {threads} threads, {dt:.1f} s (pool built by the "
+         f"oracle, untimed: {build_s:.1f} s)"),
+        tokens_per_s=round(passes * n / dt, 3))
+
+
+def cpu_baseline_prefill(w, budget_s, rows_wanted=4096):
+    """The fp64 oracle on a bounded sample of prefill workload ``w``: a pass is
+    ``write_ref`` of every prompt token, then ``prefill_ref`` of an evenly
+    strided sample of query rows (each row its own one-token call at its
+    position).  TFLOP/s counts the algorithmic flops of the sampled rows."""
+    import numpy as np
+    import oracle
+
+    kc, vc = w.empty_caches("zero")
+    stride = max(1, w.num_tokens // rows_wanted)
+    rows = np.arange(0, w.num_tokens, stride)
+    rng = np.random.default_rng(0)
+    rows = rows[rng.permutation(rows.size)]          # the sample's prefix spans all positions
+    seq_of = np.searchsorted(w.query_start, rows, side="right") - 1
+    pos = np.array([int(w.seq_lens[b]) - int(w.query_start[b + 1] - w.query_start[b])
+                    + int(r - w.query_start[b]) for r, b in zip(rows, seq_of)])
+
+    def one(i):
+        r, b = int(rows[i]), int(seq_of[i])
+        return oracle.prefill_ref(w.q[r:r + 1], np.array([0, 1]), kc, vc, w.block_tables[b:b + 1],
+                                  np.array([pos[i] + 1]), w.scale, "bf16")
+
+    def per_pass(_):
+        oracle.write_ref(w.k_tokens, w.v_tokens, w.slots, kc, vc)
+
+    n, passes, dt, threads, cores = _time_oracle(list(range(rows.size)), pos + 1, one, budget_s,
+                                                 per_pass)
+    flops = passes * 4 * w.head_dim * w.num_q_heads * int((pos[:n] + 1).sum())
+    return _baseline_entry(
+        round(flops / dt / 1e12, 6), "TFLOP/s", n, passes, dt, threads, cores,
+        (f"{passes} pass(es) of write_ref of all {len(w.slots)} prompt tokens + prefill_ref of "
+         f"{n} query rows (every {stride}th row, shuffled, each at its own position), fp64 "
+         f"NumPy, {threads} threads, {dt:.1f} s"),
+        prompt_tokens_per_s=round(passes * n / dt, 3))
 
 
 # --------------------------------------------------------------------------- device state
@@ -590,28 +747,46 @@ def swap_report(torch, ops, blocks=2048, reps=5):
     torch.cuda.empty_cache()
 
 
+def with_baseline(res, args, fn, *a, gpu_key="attn_kv_gbps"):
+    """Adds the oracle timed on the host (unless --no-cpu-baseline) to a report line."""
+    if not args.no_cpu_baseline:
+        base = fn(*a, args.report_cpu_seconds)
+        res["cpu_baseline"] = base
+        res["gpu_over_cpu"] = round(res[gpu_key] / base["value"], 1)
+    return res
+
+
 def report_all(torch, ops, args):
-    """One JSON line per workload other than the metric's (shorter runs)."""
+    """One JSON line per workload other than the metric's (shorter runs), each
+    with the oracle timed beside it on the host."""
     fp8_report(torch, ops, args)
-    prefill_report(torch, ops)
+    prefill_report(torch, ops, args)
     from paged_kv_cache_330_amd.workloads import PrefixSharingWorkload, make_decode_workload
     steps, warmup = 20, 3
-    for config, bs in ((2, None), (4, 32), (4, 64)):
+    # the Llama-7B MHA batch; the long-context batch at both block sizes, with
+    # the balanced schedule and with its stated 512-token partitions (64 per
+    # sequence, merged by the split-K reduce)
+    for config, bs, part in ((2, None, 0), (4, 32, 0), (4, 32, 512), (4, 64, 0), (4, 64, 512)):
         w = make_decode_workload(config, block_size=bs)
-        st = decode_step_state(torch, ops, w, args.pools, args.partition_tokens)
+        st = decode_step_state(torch, ops, w, args.pools, part)
         wall, t_copy, t_write, t_attn = time_steps(torch, st, steps, warmup)
-        res, _, _ = summary(w.name, {"seed": w.seed}, w.seq_lens, w.num_seqs, w.num_q_heads,
-                            w.num_kv_heads, w.head_dim, w.block_size, steps, wall, t_copy,
-                            t_write, t_attn)
-        print(json.dumps({"report": res}), flush=True)
+        res, _, alg = summary(w.name, {"seed": w.seed}, w.seq_lens, w.num_seqs, w.num_q_heads,
+                              w.num_kv_heads, w.head_dim, w.block_size, steps, wall, t_copy,
+                              t_write, t_attn)
+        res["schedule"] = "balanced" if part == 0 else f"partitions of {part} tokens"
+        t_call = time_decode_calls(torch, st, steps, 3 * steps)
+        res["mean_call_us"] = round(t_call * 1e3, 2)
+        res["call_alg_hbm_frac"] = round(alg / (t_call * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
         del st
         torch.cuda.empty_cache()
+        print(json.dumps({"report": with_baseline(res, args, cpu_baseline, w)}), flush=True)
     swap_report(torch, ops)
     # the prefix-sharing workload as stated (4 prompts x 8 samples) at both
     # block sizes, first divergent and last step; then 64 prompts x 8 samples
     # (512 sequences, 1.07 GB of unique K/V, 4.8 GB read by the plain decode),
     # also over FP8 pools
     cases = [(4, bs, final) for bs in (8, 16) for final in (False, True)] + [(64, 16, True)]
+    sharing_baselines = {}
     for prompts, bs, final in cases:
         kinds = [(False, False), (True, False)]
         if prompts == 64:
@@ -646,9 +821,19 @@ def report_all(torch, ops, args):
             res["unique_hbm_frac"] = round(res["unique_kv_gbps"] / HBM_PEAK_GBPS, 4)
             res["note"] = ("attn_kv_gbps counts the bytes every sequence reads (logical); "
                            "unique_kv_gbps the bytes the pool holds once")
-            print(json.dumps({"report": res}), flush=True)
             del st
             torch.cuda.empty_cache()
+            if not args.no_cpu_baseline:
+                key = (prompts, bs, final)
+                if key not in sharing_baselines:
+                    sharing_baselines[key] = cpu_baseline_sharing(
+                        args.prefix, bs, prompts, final, args.report_cpu_seconds)
+                base = sharing_baselines[key]
+                if fp8:   # the oracle over bf16 pools; the GPU figure counts 1-byte codes
+                    res["cpu_baseline_note"] = "oracle over the bf16 pools of the same step"
+                res["cpu_baseline"] = base
+                res["gpu_over_cpu"] = round(res["attn_tokens_per_s"] / base["tokens_per_s"], 1)
+            print(json.dumps({"report": res}), flush=True)
 
 
 def fp8_report(torch, ops, args, steps=20, warmup=3):
@@ -670,9 +855,10 @@ def fp8_report(torch, ops, args, steps=20, warmup=3):
     # the write reads bf16 K/V and the slots, writes 1-byte codes, reads scales
     wb = B * Hkv * D * 2 * (2 + 1) + 8 * B + 2 * 4 * B * Hkv
     res["write_gbps"] = round(wb / (statistics.median(t_write) * 1e-3) / 1e9, 2)
-    print(json.dumps({"report": res}), flush=True)
     del st
     torch.cuda.empty_cache()
+    ks, vs = w.fp8_scales(unused=1.0)
+    print(json.dumps({"report": with_baseline(res, args, cpu_baseline_fp8, w, ks, vs)}), flush=True)
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -685,7 +871,7 @@ PREFILL_WORKLOADS = [
 ]
 
 
-def prefill_report(torch, ops, reps=10):
+def prefill_report(torch, ops, args, reps=10):
     """Paged prefill of Llama-3-8B-shaped prompts (32 q / 8 kv heads, head_dim
     128, bf16, block size 16): the write of every prompt token through the
     slot mapping, then causal attention of the new tokens; then the same over
@@ -756,9 +942,10 @@ def prefill_report(torch, ops, reps=10):
             ops.pkv_check_device_errors()
             res[f"t_{label}_us"] = round(statistics.median(ts) * 1e3, 2)
         res["attn_fp8_tflops"] = round(flops / (res["t_attn_fp8_us"] * 1e-6) / 1e12, 1)
-        print(json.dumps({"report": res}), flush=True)
         del kc, vc, kt, vt, k8, v8
         torch.cuda.empty_cache()
+        res = with_baseline(res, args, cpu_baseline_prefill, w, gpu_key="attn_tflops")
+        print(json.dumps({"report": res}), flush=True)
 
 
 def main():
@@ -784,7 +971,7 @@ def main():
 
     ops.load_library()
     if args.prefill:
-        prefill_report(torch, ops)
+        prefill_report(torch, ops, args)
         return
     if args.fp8:
         fp8_report(torch, ops, args)

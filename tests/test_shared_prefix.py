@@ -193,8 +193,11 @@ def test_shared_decode_bf16_output(ops):
     out = run_shared(ops, t, batch, batch.groups, out_dtype=torch.bfloat16)
     got = out.float().cpu().numpy().astype(np.float64)
     ref = batch.reference()
-    # bf16 rounding of the output adds at most half an ulp of |ref| (< 2^-8 |ref|)
-    assert_close(got, ref, "bf16 output", tol=TOL + float(np.abs(ref).max()) * 2.0 ** -8)
+    # bf16 rounding of the output adds at most half a bf16 ulp of each value
+    half_ulp = np.ldexp(1.0, np.frexp(np.abs(ref))[1] - 9)
+    excess = np.abs(got - ref) - (TOL + half_ulp)
+    say(f"  bf16 output: max excess over 2e-3 + half ulp {excess.max():.3e}")
+    assert np.isfinite(got).all() and (excess <= 0).all()
 
 
 def test_shared_decode_workspace_reuse(ops):
