@@ -177,6 +177,31 @@ int pkv_attention_decode(void* out, int32_t out_dtype, const void* q,
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pkv_attention_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Arguments, result and errors are those
+ * of pkv_attention_decode, whose kernels it runs; the partial results go to
+ * a scratch array the library holds per device: 32 MiB (33554432 bytes),
+ * placed when the library is loaded on that device and held until the
+ * process ends.  The call allocates nothing and calls no allocating routine.
+ * Sizes whose pkv_attention_workspace_bytes(...) exceeds 33554432 return
+ * PKV_ERR_WORKSPACE before any launch (the batch-256 GQA decode with 32 query
+ * heads needs 8.1 MiB, 8 sequences of 32768 tokens with 64 query heads
+ * 16.3 MiB with either schedule).
+ * The scratch array keeps the last call's contents; nothing in it has to
+ * start at zero.  Every call on one device shares that device's array:
+ * calls that overlap in time on one device (on different streams, or from
+ * different threads without ordering) race and must not be issued.
+ */
+int pkv_attention_decode_noalloc(void* out, int32_t out_dtype, const void* q,
+                                 const void* k_cache, const void* v_cache,
+                                 const pkv_cache_desc* cache,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* seq_lens, int32_t num_seqs,
+                                 int32_t num_q_heads, float scale, int32_t partition_tokens,
+                                 void* stream);
+
+/*
  * Bytes of device workspace pkv_attention_decode_shared (bf16 descriptor) or
  * pkv_attention_decode_shared_fp8 (FP8 descriptor) needs: 0 for arguments
  * that call would reject, with pkv_last_error() saying why, and for

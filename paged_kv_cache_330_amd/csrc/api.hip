@@ -65,6 +65,31 @@ int error_word(unsigned** out) {
   return PKV_OK;
 }
 
+// Workspace of pkv_attention_decode_noalloc: one array per device, for
+// callers that cannot allocate.  In host code `scratch` names a host-side
+// stand-in, not device memory: host code uses only the device address that
+// hipGetSymbolAddress returns for the current device (g_scratch_ptr).
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;  // 32 MiB
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+void* g_scratch_ptr[kMaxDevices];  // guarded by g_error_mutex
+
+// Device address of the current device's `scratch` (looked up once per device).
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(PKV_ERR_HIP, "device ordinal %d too large", dev);
+  std::lock_guard<std::mutex> lock(g_error_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 int elem_bytes(int32_t dtype) { return dtype == PKV_F32 ? 4 : dtype == PKV_BF16 ? 2 : 1; }
@@ -287,6 +312,42 @@ int attach_workspace(void* workspace, size_t workspace_bytes, size_t need,
   return PKV_OK;
 }
 
+// Both bf16/fp32 decode calls.  no_alloc: the workspace is this device's
+// `scratch` array (workspace/workspace_bytes unused); sizes past it are
+// rejected before any HIP call.
+int decode_common(void* out, int32_t out_dtype, const void* q, const void* k_cache,
+                  const void* v_cache, const pkv_cache_desc* cache, const int32_t* block_tables,
+                  int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                  int32_t num_q_heads, float scale, int32_t partition_tokens, void* workspace,
+                  size_t workspace_bytes, bool no_alloc, void* stream) {
+  Plan plan;
+  PKV_TRY(make_plan(cache, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, &plan));
+  PKV_TRY(check_not_fp8(cache, no_alloc ? "pkv_attention_decode_noalloc" : "pkv_attention_decode"));
+  PKV_TRY(check_decode_scalars(cache, num_q_heads, out_dtype, scale));
+  if (no_alloc && plan.workspace > kNoAllocScratchBytes)
+    return fail(PKV_ERR_WORKSPACE,
+                "pkv_attention_decode_noalloc: these sizes need %zu bytes of scratch, more than "
+                "the %zu bytes the library holds per device",
+                plan.workspace, kNoAllocScratchBytes);
+  if (num_seqs == 0) return PKV_OK;
+  pkv::DecodeArgs a{};
+  PKV_TRY(fill_decode_args(out, out_dtype, q, k_cache, v_cache, cache, block_tables,
+                           max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, scale, &a));
+  if (no_alloc && plan.workspace > 0) {
+    PKV_TRY(scratch_address(&workspace));
+    workspace_bytes = kNoAllocScratchBytes;
+  }
+  PKV_TRY(attach_workspace(workspace, workspace_bytes, plan.workspace, plan.layout, &a));
+  PKV_TRY(error_word(&a.err));
+  a.part_tokens = plan.part;
+  a.max_parts = static_cast<int32_t>(plan.max_parts);
+  a.slices = plan.slices;
+  hipError_t e = pkv::launch_decode(a, cache->dtype == PKV_BF16, cache->head_dim,
+                                    cache->block_size, num_q_heads / cache->num_kv_heads,
+                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "attention_decode launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -393,23 +454,21 @@ int pkv_attention_decode(void* out, int32_t out_dtype, const void* q, const void
                          float scale, int32_t partition_tokens, void* workspace,
                          size_t workspace_bytes, void* stream) {
   g_last_error.clear();
-  Plan plan;
-  PKV_TRY(make_plan(cache, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, &plan));
-  PKV_TRY(check_not_fp8(cache, "pkv_attention_decode"));
-  PKV_TRY(check_decode_scalars(cache, num_q_heads, out_dtype, scale));
-  if (num_seqs == 0) return PKV_OK;
-  pkv::DecodeArgs a{};
-  PKV_TRY(fill_decode_args(out, out_dtype, q, k_cache, v_cache, cache, block_tables,
-                           max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, scale, &a));
-  PKV_TRY(attach_workspace(workspace, workspace_bytes, plan.workspace, plan.layout, &a));
-  PKV_TRY(error_word(&a.err));
-  a.part_tokens = plan.part;
-  a.max_parts = static_cast<int32_t>(plan.max_parts);
-  a.slices = plan.slices;
-  hipError_t e = pkv::launch_decode(a, cache->dtype == PKV_BF16, cache->head_dim,
-                                    cache->block_size, num_q_heads / cache->num_kv_heads,
-                                    static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? PKV_OK : hip_fail(e, "attention_decode launch");
+  return decode_common(out, out_dtype, q, k_cache, v_cache, cache, block_tables,
+                       max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, scale,
+                       partition_tokens, workspace, workspace_bytes, false, stream);
+}
+
+int pkv_attention_decode_noalloc(void* out, int32_t out_dtype, const void* q,
+                                 const void* k_cache, const void* v_cache,
+                                 const pkv_cache_desc* cache, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                 int32_t num_seqs, int32_t num_q_heads, float scale,
+                                 int32_t partition_tokens, void* stream) {
+  g_last_error.clear();
+  return decode_common(out, out_dtype, q, k_cache, v_cache, cache, block_tables,
+                       max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, scale,
+                       partition_tokens, nullptr, 0, true, stream);
 }
 
 size_t pkv_attention_shared_workspace_bytes(const pkv_cache_desc* cache, int32_t num_seqs,

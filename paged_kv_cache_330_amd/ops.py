@@ -88,6 +88,8 @@ def load_library() -> ctypes.CDLL:
     lib.pkv_attention_workspace_bytes.restype = SZ
     lib.pkv_attention_decode.argtypes = [P, I32, P, P, P, D, P, I32, P, I32, I32,
                                          ctypes.c_float, I32, P, SZ, P]
+    lib.pkv_attention_decode_noalloc.argtypes = [P, I32, P, P, P, D, P, I32, P, I32, I32,
+                                                 ctypes.c_float, I32, P]
     lib.pkv_attention_shared_workspace_bytes.argtypes = [D, I32, I32, I32]
     lib.pkv_attention_shared_workspace_bytes.restype = SZ
     lib.pkv_attention_decode_shared.argtypes = [P, I32, P, P, P, D, P, I32, P, I32, I32,
@@ -106,6 +108,7 @@ def load_library() -> ctypes.CDLL:
     lib.pkv_last_error.restype = ctypes.c_char_p
     lib.pkv_check_device_errors.argtypes = [P]
     for name in ("pkv_kv_write", "pkv_block_copy", "pkv_block_transfer", "pkv_attention_decode",
+                 "pkv_attention_decode_noalloc",
                  "pkv_attention_decode_shared", "pkv_attention_prefill", "pkv_kv_write_fp8",
                  "pkv_attention_decode_fp8", "pkv_attention_prefill_fp8", "pkv_block_copy_fp8",
                  "pkv_block_transfer_fp8", "pkv_attention_decode_shared_fp8",
@@ -272,6 +275,31 @@ def pkv_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tens
         _ptr(out), _DTYPES[out.dtype], _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
         _ptr(block_tables), mb, _ptr(seq_lens), B, Hq, float(scale), partition_tokens,
         _ptr(workspace), wbytes, _stream()))
+    return out
+
+
+def pkv_attention_decode_noalloc(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                                 v_cache: torch.Tensor, block_tables: torch.Tensor,
+                                 seq_lens: torch.Tensor, scale: float,
+                                 partition_tokens: int = 0) -> torch.Tensor:
+    """``pkv_attention_decode`` with the library's per-device scratch array as
+    its workspace: nothing is allocated.  Calls on one device must not overlap."""
+    desc = _desc(k_cache, v_cache)
+    _need(q, "q", dtype=k_cache.dtype, ndim=3)
+    _need(out, "out", ndim=3)
+    if out.dtype not in _DTYPES:
+        raise TypeError("out must be float32 or bfloat16")
+    _need(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _need(seq_lens, "seq_lens", dtype=torch.int32, ndim=1)
+    B, Hq, D = q.shape
+    if tuple(out.shape) != (B, Hq, D) or D != desc.head_dim:
+        raise ValueError("out/q shapes do not match [B, Hq, head_dim]")
+    if block_tables.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("block_tables/seq_lens must have B rows")
+    _check(load_library().pkv_attention_decode_noalloc(
+        _ptr(out), _DTYPES[out.dtype], _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
+        _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), B, Hq, float(scale),
+        partition_tokens, _stream()))
     return out
 
 

@@ -399,3 +399,34 @@ def test_fp8_shared_prefix_validation(lib):
     # and the bf16 shared call takes no FP8 pools
     assert shared(lib, desc=d8) == UNSUPPORTED
     assert "pkv_attention_decode_shared_fp8" in ops.pkv_last_error()
+
+
+def decode_noalloc(lib, **kw):
+    a = dict(out=P(), out_dtype=0, q=P(), k=P(), v=P(), desc=desc(), bt=P(), mb=32, sl=P(),
+             B=4, Hq=32, scale=0.088, part=0)
+    a.update(kw)
+    return lib.pkv_attention_decode_noalloc(a["out"], a["out_dtype"], a["q"], a["k"], a["v"],
+                                            ctypes.byref(a["desc"]), a["bt"], a["mb"], a["sl"],
+                                            a["B"], a["Hq"], a["scale"], a["part"], P(0))
+
+
+def test_noalloc_decode_rejects_sizes_past_its_scratch(lib):
+    # The partials of the partition grid grow with B * Hq * partitions: 64
+    # sequences of up to 64 blocks of 64 tokens at 64-token partitions need
+    # 64 * 64 * 64 rows of 520 bytes (~136 MB), more than the 32 MiB array.
+    d64 = desc(bs=64)
+    need = ws_bytes(lib, d64, 64, 64, 64, 64)
+    assert need > 32 << 20
+    assert decode_noalloc(lib, desc=d64, B=64, Hq=64, mb=64, part=64) == WORKSPACE
+    msg = ops.pkv_last_error()
+    assert str(need) in msg and str(32 << 20) in msg
+    # the batch-256 GQA and 8 x 32768-token long-context sizes fit
+    assert ws_bytes(lib, desc(), 256, 32, 512, 0) <= 32 << 20
+    d32 = desc(bs=32)
+    assert ws_bytes(lib, d32, 8, 64, 1024, 0) <= 32 << 20
+    assert ws_bytes(lib, d32, 8, 64, 1024, 512) <= 32 << 20
+    # the same host checks as pkv_attention_decode, before any HIP call
+    assert decode_noalloc(lib, Hq=24) == UNSUPPORTED
+    assert decode_noalloc(lib, part=48) == INVALID
+    assert decode_noalloc(lib, q=P(0)) == INVALID
+    assert decode_noalloc(lib, B=0) == OK
