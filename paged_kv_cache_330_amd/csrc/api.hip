@@ -562,7 +562,6 @@ int shared_common(void* out, int32_t out_dtype, const void* q, const void* k_cac
   sa.group_seqs = group_seqs;
   sa.group_lens = group_lens;
   sa.num_groups = num_groups;
-  sa.min_chunks = PKV_SHARED_MIN_CHUNKS;
   sa.prefix_rows = plan.prefix_rows;
   hipError_t e = pkv::launch_shared_decode(sa, cache->block_size,
                                            num_q_heads / cache->num_kv_heads,

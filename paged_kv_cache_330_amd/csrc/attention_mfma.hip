@@ -20,12 +20,12 @@ namespace {
 // dispatched from the last to the first so that the full partitions of long
 // sequences start early and the short tails of short ones fill the end.
 // ----------------------------------------------------------------------------
-template <int G, int BS, int TC, bool F8>
+template <int G, int BS, bool F8>
 __global__ __launch_bounds__(kMaxWaves * 64) void decode_mfma_kernel(DecodeArgs a) {
   static_assert(16 % G == 0, "group must divide 16");
   __shared__ int s_bt[kMaxPartitionTokens / BS + 1];
-  __shared__ u32x4_t s_kt[PKV_K_VIA_LDS ? kMaxWaves * 16 * kKRowPad : 1];
-  __shared__ u32x4_t s_vt[kPvOnMfma<G> ? kMaxWaves * 16 * TC * kVRowPad : 1];
+  __shared__ u32x4_t s_kt[kMaxWaves * 16 * kKRowPad];
+  __shared__ u32x4_t s_vt[kPvOnMfma<G> ? kMaxWaves * 16 * kVRowPad : 1];
   const int kh = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kvh = blockIdx.x * kh + wave;
@@ -41,8 +41,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mfma_kernel(DecodeArgs 
   load_query<G>(a, b, kvh, lane & 15, lane >> 4, qop);
   WaveState<G> st;
   st.reset();
-  attend_range<G, BS, TC, F8>(a, s_bt, s_kt + (PKV_K_VIA_LDS ? wave * 16 * kKRowPad : 0),
-                          s_vt + (kPvOnMfma<G> ? wave * 16 * TC * kVRowPad : 0), b, kvh, pt.begin,
+  attend_range<G, BS, F8>(a, s_bt, s_kt + wave * 16 * kKRowPad,
+                          s_vt + (kPvOnMfma<G> ? wave * 16 * kVRowPad : 0), b, kvh, pt.begin,
                           pt.end, qop, st);
   Sink sink{nullptr, nullptr, nullptr, 0, 0};
   if (pt.count > 1) {
@@ -71,13 +71,12 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mfma_kernel(DecodeArgs 
 // sequence (its first piece); its merge descriptor ws_desc[slice] names that
 // sequence and the slice of its first piece, or -1.
 // ----------------------------------------------------------------------------
-template <int G, int BS, int TC, bool F8>
-__global__ __launch_bounds__(kMaxWaves * 64) PKV_BALANCED_OCCUPANCY void decode_balanced_kernel(
-    DecodeArgs a) {
+template <int G, int BS, bool F8>
+__global__ __launch_bounds__(kMaxWaves * 64) void decode_balanced_kernel(DecodeArgs a) {
   static_assert(16 % G == 0, "group must divide 16");
   __shared__ int s_bt[kMaxPartitionTokens / BS + 1];
-  __shared__ u32x4_t s_kt[PKV_K_VIA_LDS ? kMaxWaves * 16 * kKRowPad : 1];
-  __shared__ u32x4_t s_vt[kPvOnMfma<G> ? kMaxWaves * 16 * TC * kVRowPad : 1];
+  __shared__ u32x4_t s_kt[kMaxWaves * 16 * kKRowPad];
+  __shared__ u32x4_t s_vt[kPvOnMfma<G> ? kMaxWaves * 16 * kVRowPad : 1];
   __shared__ int s_cc[kMaxBalancedSeqs + 1];
   __shared__ int s_len[kMaxBalancedSeqs];  // clamped sequence lengths
   __shared__ int s_wsum[kMaxWaves];
@@ -154,9 +153,9 @@ __global__ __launch_bounds__(kMaxWaves * 64) PKV_BALANCED_OCCUPANCY void decode_
     load_query<G>(a, b, kvh, lane & 15, lane >> 4, qop);
     WaveState<G> st;
     st.reset();
-    attend_range<G, BS, TC, F8>(a, s_bt, s_kt + (PKV_K_VIA_LDS ? wave * 16 * kKRowPad : 0),
-                            s_vt + (kPvOnMfma<G> ? wave * 16 * TC * kVRowPad : 0), b, kvh, tok_begin,
-                            tok_end, qop, st, (PKV_WAVE_BALANCE && nw == 8) ? s_prog : nullptr);
+    attend_range<G, BS, F8>(a, s_bt, s_kt + wave * 16 * kKRowPad,
+                            s_vt + (kPvOnMfma<G> ? wave * 16 * kVRowPad : 0), b, kvh, tok_begin,
+                            tok_end, qop, st, nw == 8 ? s_prog : nullptr);
     Sink sink{nullptr, nullptr, nullptr, 0, 0};
     if (!(first && last))
       sink = Sink{a.ws_acc, a.ws_max, a.ws_sum,
@@ -242,14 +241,13 @@ __global__ __launch_bounds__(kMaxWaves * 64) void balanced_reduce_kernel(DecodeA
 
 template <int G, bool F8>
 hipError_t launch_partitions_g(const DecodeArgs& a, int block_size, int kh, hipStream_t s) {
-  constexpr int TC = F8 ? PKV_FP8_TILE_CHUNKS : PKV_MFMA_TILE_CHUNKS;
   const dim3 grid(a.num_kv_heads / kh, a.num_seqs, a.max_parts);
   const dim3 block(kh * 64);
   switch (block_size) {
-    case 8: decode_mfma_kernel<G, 8, TC, F8><<<grid, block, 0, s>>>(a); break;
-    case 16: decode_mfma_kernel<G, 16, TC, F8><<<grid, block, 0, s>>>(a); break;
-    case 32: decode_mfma_kernel<G, 32, TC, F8><<<grid, block, 0, s>>>(a); break;
-    case 64: decode_mfma_kernel<G, 64, TC, F8><<<grid, block, 0, s>>>(a); break;
+    case 8: decode_mfma_kernel<G, 8, F8><<<grid, block, 0, s>>>(a); break;
+    case 16: decode_mfma_kernel<G, 16, F8><<<grid, block, 0, s>>>(a); break;
+    case 32: decode_mfma_kernel<G, 32, F8><<<grid, block, 0, s>>>(a); break;
+    case 64: decode_mfma_kernel<G, 64, F8><<<grid, block, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -257,14 +255,13 @@ hipError_t launch_partitions_g(const DecodeArgs& a, int block_size, int kh, hipS
 
 template <int G, bool F8>
 hipError_t launch_balanced_g(const DecodeArgs& a, int block_size, int kh, hipStream_t s) {
-  constexpr int TC = F8 ? PKV_FP8_TILE_CHUNKS : PKV_MFMA_TILE_CHUNKS;
   const dim3 grid(a.num_kv_heads / kh, a.slices);
   const dim3 block(kh * 64);
   switch (block_size) {
-    case 8: decode_balanced_kernel<G, 8, TC, F8><<<grid, block, 0, s>>>(a); break;
-    case 16: decode_balanced_kernel<G, 16, TC, F8><<<grid, block, 0, s>>>(a); break;
-    case 32: decode_balanced_kernel<G, 32, TC, F8><<<grid, block, 0, s>>>(a); break;
-    case 64: decode_balanced_kernel<G, 64, TC, F8><<<grid, block, 0, s>>>(a); break;
+    case 8: decode_balanced_kernel<G, 8, F8><<<grid, block, 0, s>>>(a); break;
+    case 16: decode_balanced_kernel<G, 16, F8><<<grid, block, 0, s>>>(a); break;
+    case 32: decode_balanced_kernel<G, 32, F8><<<grid, block, 0, s>>>(a); break;
+    case 64: decode_balanced_kernel<G, 64, F8><<<grid, block, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
@@ -288,7 +285,7 @@ namespace {
 template <bool F8>
 hipError_t launch_mfma_typed(const DecodeArgs& a, int block_size, int group, hipStream_t s) {
   if (a.slices > 0) {
-    const int kh = balanced_waves_per_group(a.num_kv_heads);
+    const int kh = mfma_waves_per_group(a.num_kv_heads);
     if (a.num_seqs > kMaxBalancedSeqs) return hipErrorInvalidValue;
     switch (group) {
       case 1: return launch_balanced_g<1, F8>(a, block_size, kh, s);

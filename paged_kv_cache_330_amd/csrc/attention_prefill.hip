@@ -41,38 +41,20 @@
 namespace pkv {
 namespace {
 
-#ifndef PKV_PREFILL_CHUNKS
-#define PKV_PREFILL_CHUNKS 2  // 16-token chunks per shared K/V tile
-#endif
-#ifndef PKV_PREFILL_SCALAR_BASE
-#define PKV_PREFILL_SCALAR_BASE 1  // block_size >= 16: chunk address in scalar registers, 32-bit lane offsets
-#endif
-#ifndef PKV_PREFILL_FOLD_SCALE
-#define PKV_PREFILL_FOLD_SCALE 1   // bf16: score factor applied in the exponent's fused multiply-add
-#endif
-#ifndef PKV_PREFILL_MFMA_PRIO
-#define PKV_PREFILL_MFMA_PRIO 1  // issue priority 1 while a wave issues its matrix products
-#endif
-#ifndef PKV_PREFILL_PV32
-#define PKV_PREFILL_PV32 1    // P.V of chunk pairs with the 16x16x32 product
-#endif
-
 constexpr int kCols = 16 * kSharedSets;  // query columns of a wave
 constexpr int kItemWaves = 4;            // waves of a work item, sharing each K/V tile
 constexpr int kItemThreads = kItemWaves * 64;
-constexpr int kTC = PKV_PREFILL_CHUNKS;  // chunks per tile
+constexpr int kTC = 2;                   // 16-token chunks per shared K/V tile
 constexpr int kTileRows = 16 * kTC;      // tokens per tile
 static_assert(kItemThreads == 16 * 16, "one 16-byte unit of 16 rows per lane and chunk");
 
 constexpr int kXcds = 8;  // XCDs of the device; workgroups go round-robin over them
 
-#ifndef PKV_PREFILL_STALE_MAX
-#define PKV_PREFILL_STALE_MAX 8  // log2 headroom of the running max (0: move it with every tile max)
-#endif
+constexpr float kStaleMax = 8.f;  // log2 headroom of the running max
 
 // Online-softmax step of one column that moves the running max m only when
-// the tile's maximum exceeds it by more than 2^PKV_PREFILL_STALE_MAX.  Until
-// then the probabilities exp2(x - m) stay below 2^PKV_PREFILL_STALE_MAX
+// the tile's maximum exceeds it by more than 2^kStaleMax = 2^8.  Until
+// then the probabilities exp2(x - m) stay below 2^8
 // (far from the fp32 range, and split into bf16 hi + lo as before) and the
 // accumulators need no rescaling.  The normalised result o / l does not
 // depend on the m it was accumulated with, so only rounding changes; with a
@@ -82,7 +64,7 @@ constexpr int kXcds = 8;  // XCDs of the device; workgroups go round-robin over 
 template <int TC>
 __device__ __forceinline__ float softmax_update_stale(float (&x)[TC][4], float mt, float& m,
                                                       float& l) {
-  const float m_new = mt > m + float(PKV_PREFILL_STALE_MAX) ? mt : m;  // m = -inf: takes mt
+  const float m_new = mt > m + kStaleMax ? mt : m;  // m = -inf: takes mt
   const float alpha = exp2_hw(m - m_new);
   m = m_new;
   float psum = 0.f;
@@ -105,7 +87,7 @@ template <int TC>
 __device__ __forceinline__ float softmax_update_stale_raw(float (&x)[TC][4], float mt, float sl,
                                                           float& m, float& l) {
   const float mts = mt * sl;
-  const float m_new = mts > m + float(PKV_PREFILL_STALE_MAX) ? mts : m;  // m = -inf: takes mts
+  const float m_new = mts > m + kStaleMax ? mts : m;  // m = -inf: takes mts
   const float alpha = exp2_hw(m - m_new);
   m = m_new;
   float psum = 0.f;
@@ -211,7 +193,7 @@ __global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa
   // bf16 value negates every product and sum), and sl = 0 is raised to the
   // smallest normal float, which leaves every exponent's rounding unchanged
   // (|score| * 2^-126 is far below half an ulp of the maximum's shift).
-  constexpr bool kFold = !F8 && PKV_PREFILL_FOLD_SCALE;
+  constexpr bool kFold = !F8;
   float slf = a.scale_log2e;
   if constexpr (kFold) {
     if (slf < 0.f) {
@@ -259,7 +241,7 @@ __global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa
     auto load_units = [&](int tt, TileUnits<F8>& u) {
 #pragma unroll
       for (int c = 0; c < kTC; ++c) {
-        if constexpr (BS >= 16 && PKV_PREFILL_SCALAR_BASE) {
+        if constexpr (BS >= 16) {
           // The chunk lies in one block: its address is wave-uniform and a
           // lane adds the 32-bit offset of its row, clamped to the window's
           // last token.  A chunk wholly past the end re-reads the last chunk
@@ -278,19 +260,19 @@ __global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa
             u.k[c] = *reinterpret_cast<const u32x4_t*>(kpool + first + off);
             u.v[c] = *reinterpret_cast<const u32x4_t*>(vpool + first + off);
           }
-          continue;
-        }
-        const int tok = min(tt + 16 * c + urow, wend - 1);
-        const int phys = s_bt[tok / BS - blk0];
-        const int64_t row = ((int64_t)phys * BS + (tok & (BS - 1))) * tok_stride;
-        if constexpr (F8) {
-          u.k[c] = *reinterpret_cast<const u32x2_t*>(kbase8 + row);
-          u.v[c] = *reinterpret_cast<const u32x2_t*>(vbase8 + row);
-          u.ks[c] = a.k_scale[(int64_t)phys * a.num_kv_heads + kvh];
-          u.vs[c] = a.v_scale[(int64_t)phys * a.num_kv_heads + kvh];
         } else {
-          u.k[c] = *reinterpret_cast<const u32x4_t*>(kbase + row);
-          u.v[c] = *reinterpret_cast<const u32x4_t*>(vbase + row);
+          const int tok = min(tt + 16 * c + urow, wend - 1);
+          const int phys = s_bt[tok / BS - blk0];
+          const int64_t row = ((int64_t)phys * BS + (tok & (BS - 1))) * tok_stride;
+          if constexpr (F8) {
+            u.k[c] = *reinterpret_cast<const u32x2_t*>(kbase8 + row);
+            u.v[c] = *reinterpret_cast<const u32x2_t*>(vbase8 + row);
+            u.ks[c] = a.k_scale[(int64_t)phys * a.num_kv_heads + kvh];
+            u.vs[c] = a.v_scale[(int64_t)phys * a.num_kv_heads + kvh];
+          } else {
+            u.k[c] = *reinterpret_cast<const u32x4_t*>(kbase + row);
+            u.v[c] = *reinterpret_cast<const u32x4_t*>(vbase + row);
+          }
         }
       }
     };
@@ -315,9 +297,7 @@ __global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa
     auto compute = [&](int buf, int tt) {
       const u32x4_t* kt = s_k[buf];
       float x[kSharedSets][kTC][4], mt[kSharedSets], alpha[kSharedSets];
-#if PKV_PREFILL_MFMA_PRIO
       __builtin_amdgcn_s_setprio(1);  // Q.K^T: this wave's products go first
-#endif
 #pragma unroll
       for (int c = 0; c < kTC; ++c) {
         u32x4_t kop[4];
@@ -337,9 +317,7 @@ __global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa
           for (int i = 0; i < 4; ++i) x[m][c][i] = kFold ? sacc[i] : sacc[i] * sl;
         }
       }
-#if PKV_PREFILL_MFMA_PRIO
       __builtin_amdgcn_s_setprio(0);  // softmax: the other wave's products may go first
-#endif
       if (tt + kTileRows > mask_from) {  // the causal diagonal or the window's end
 #pragma unroll
         for (int c = 0; c < kTC; ++c)
@@ -373,27 +351,15 @@ __global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa
         }
       }
       rescale_lazy<kSharedSets>(alpha, st);
-#if PKV_PREFILL_MFMA_PRIO
       __builtin_amdgcn_s_setprio(1);  // P.V
-#endif
       const uint16_t* vt = reinterpret_cast<const uint16_t*>(s_v[buf]);
-#if PKV_PREFILL_PV32
+      static_assert(kTC % 2 == 0, "P.V takes the chunks of a tile in pairs");
 #pragma unroll
-      for (int c = 0; c + 1 < kTC; c += 2)
+      for (int c = 0; c < kTC; c += 2)
         pv_pair_from_lds<kTC, kSharedSets>(vt + 16 * c * kVRowPad * 8,
                                            vt + 16 * (c + 1) * kVRowPad * 8, c, c + 1, x, col,
                                            qr, st);
-      if constexpr (kTC & 1)
-        pv_from_lds<kTC, kSharedSets>(vt + 16 * (kTC - 1) * kVRowPad * 8, kTC - 1, x, col, qr,
-                                      st);
-#else
-#pragma unroll
-      for (int c = 0; c < kTC; ++c)
-        pv_from_lds<kTC, kSharedSets>(vt + 16 * c * kVRowPad * 8, c, x, col, qr, st);
-#endif
-#if PKV_PREFILL_MFMA_PRIO
       __builtin_amdgcn_s_setprio(0);
-#endif
     };
     // Two tiles in flight: registers a and b alternate, tile t is computed
     // from LDS buffer t & 1 while tiles t + 1 (staged next) and t + 2 load.

@@ -25,7 +25,7 @@
 // sequence's own tokens with the G heads of its kv head, as in the plain
 // decode.  The 16-token chunks of all prefix streams, then of all tail
 // streams, are laid end to end and every workgroup takes an equal slice
-// (at least PKV_SHARED_MIN_CHUNKS chunks), as in the balanced schedule of the
+// (at least one chunk), as in the balanced schedule of the
 // plain decode.  Every workgroup derives the whole layout from the group
 // description and seq_lens in LDS.
 //
@@ -81,14 +81,13 @@ __device__ __forceinline__ void store_columns(const DecodeArgs& a, MfmaState<NS>
 }
 
 // Workgroup (kv-head group, slice); wave w owns kv head blockIdx.x * KH + w.
-template <int G, int BS, int TC, bool F8>
+template <int G, int BS, bool F8>
 __global__ __launch_bounds__(kMaxWaves * 64) void decode_shared_kernel(SharedArgs sa) {
   static_assert(16 % G == 0, "group must divide 16");
-  static_assert(TC == 1, "V tiles hold one 16-row chunk per wave (LDS is nearly full)");
   constexpr int MPS = kMembers<G>;
   const DecodeArgs& a = sa.d;
   __shared__ int s_bt[kMaxPartitionTokens / BS + 1];
-  __shared__ u32x4_t s_kt[PKV_K_VIA_LDS ? kMaxWaves * 16 * kKRowPad : 1];
+  __shared__ u32x4_t s_kt[kMaxWaves * 16 * kKRowPad];
   __shared__ u32x4_t s_vt[kMaxWaves * 16 * kVRowPad];  // prefix pieces: P.V on the matrix cores
   __shared__ int s_goff[kMaxBalancedSeqs + 1];  // member offsets of the groups
   __shared__ int s_gsp[kMaxBalancedSeqs + 1];   // first prefix stream of each group
@@ -109,7 +108,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_shared_kernel(SharedArg
   const int B = a.num_seqs;
   const bool reporter = blockIdx.x == 0 && slice == 0;
   const int cap = a.max_blocks_per_seq * BS;
-  u32x4_t* k_lds = s_kt + (PKV_K_VIA_LDS ? wave * 16 * kKRowPad : 0);
+  u32x4_t* k_lds = s_kt + wave * 16 * kKRowPad;
   u32x4_t* v_lds = s_vt + wave * 16 * kVRowPad;
 
   // 1. One round of independent global loads: group offsets, shared lengths,
@@ -119,7 +118,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_shared_kernel(SharedArg
   if (threadIdx.x == 0) s_bad = 0;
   if (threadIdx.x < kMaxWaves) s_prog[threadIdx.x] = 0;
   __syncthreads();
-  int* prog = (PKV_WAVE_BALANCE && blockDim.x == 8 * 64) ? s_prog : nullptr;
+  int* prog = blockDim.x == 8 * 64 ? s_prog : nullptr;
   for (int g = threadIdx.x; g <= NG && NG > 0; g += blockDim.x) {
     const int o = sa.group_offsets[g];
     s_goff[g] = o;
@@ -182,7 +181,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_shared_kernel(SharedArg
     const int b = st - NPS;
     return s_len[b] > s_tail[b] ? (s_len[b] - s_tail[b] + 15) >> 4 : 0;
   });
-  const int per = max(sa.min_chunks, (total + S - 1) / S);
+  const int per = max(1, (total + S - 1) / S);
 
   // 6. Merge descriptors, one workgroup: (merge needed, tail slices [tf, tl],
   //    prefix stream or -1, its slices [pf, pl], the member's first column).
@@ -247,9 +246,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_shared_kernel(SharedArg
       }
       MfmaState<kSharedSets> ps;
       ps.reset();
-      attend_table<BS, TC, true, F8>(a, s_bt, k_lds, v_lds,
-                                 a.block_tables + (int64_t)lead * a.max_blocks_per_seq,
-                                 q + ((int64_t)lead * a.num_q_heads + kvh * G) * kD, kvh,
+      attend_table<BS, true, F8>(a, s_bt, k_lds, v_lds,
+                                 a.block_tables + (int64_t)lead * a.max_blocks_per_seq, kvh,
                                  (c - cs) * 16, (c_end - cs) * 16, qop, ps,
                                  TableCheck{sa.group_seqs + m0, nm}, WindowTokens{}, prog);
       store_columns(a, ps, ((int64_t)(st + slice) * a.num_kv_heads + kvh) * kCols, nm * G);
@@ -262,7 +260,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_shared_kernel(SharedArg
       load_query<G>(a, b, kvh, col, qr, qop);
       WaveState<G> ws;
       ws.reset();
-      attend_range<G, BS, TC, F8>(a, s_bt, k_lds, v_lds, b, kvh, T + (c - cs) * 16,
+      attend_range<G, BS, F8>(a, s_bt, k_lds, v_lds, b, kvh, T + (c - cs) * 16,
                                   min(T + (c_end - cs) * 16, L), qop, ws, prog);
       Sink sink{nullptr, nullptr, nullptr, 0, 0};
       if (!(T == 0 && c == cs && c_end == ce))
@@ -319,14 +317,13 @@ __global__ __launch_bounds__(256) void shared_merge_kernel(SharedArgs sa) {
 
 template <int G, bool F8>
 hipError_t launch_shared_g(const SharedArgs& a, int block_size, int kh, hipStream_t s) {
-  constexpr int TC = 1;  // one chunk per tile: the V tiles are sized for 16 rows
   const dim3 grid(a.d.num_kv_heads / kh, a.d.slices);
   const dim3 block(kh * 64);
   switch (block_size) {
-    case 8: decode_shared_kernel<G, 8, TC, F8><<<grid, block, 0, s>>>(a); break;
-    case 16: decode_shared_kernel<G, 16, TC, F8><<<grid, block, 0, s>>>(a); break;
-    case 32: decode_shared_kernel<G, 32, TC, F8><<<grid, block, 0, s>>>(a); break;
-    case 64: decode_shared_kernel<G, 64, TC, F8><<<grid, block, 0, s>>>(a); break;
+    case 8: decode_shared_kernel<G, 8, F8><<<grid, block, 0, s>>>(a); break;
+    case 16: decode_shared_kernel<G, 16, F8><<<grid, block, 0, s>>>(a); break;
+    case 32: decode_shared_kernel<G, 32, F8><<<grid, block, 0, s>>>(a); break;
+    case 64: decode_shared_kernel<G, 64, F8><<<grid, block, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();

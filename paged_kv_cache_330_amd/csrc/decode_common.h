@@ -2,8 +2,6 @@
 // attention_valu.hip).  Host code never includes this file.
 #pragma once
 
-#include <utility>
-
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -16,34 +14,12 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  [&]<int... I>(std::integer_sequence<int, I...>) {
-    (f(std::integral_constant<int, I>{}), ...);
-  }(std::make_integer_sequence<int, N>{});
-}
-
 // 2^x on the hardware exp unit; scores are pre-multiplied by log2(e).
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // exp2(m_old - m_new) with an empty side (-inf) weighted 0 even when both are -inf.
 __device__ __forceinline__ float rescale(float m_old, float m_new) {
   return m_old == -INFINITY ? 0.f : exp2_hw(m_old - m_new);
-}
-
-// Value of the lane R places further round this lane's 16-lane DPP row
-// (row_ror:R).  Every lane of the row must be active.
-template <int R>
-__device__ __forceinline__ int row_ror(int x) {
-  if constexpr (R == 0) {
-    return x;
-  } else {
-    return __builtin_amdgcn_update_dpp(0, x, 0x120 + R, 0xF, 0xF, false);
-  }
-}
-template <int R>
-__device__ __forceinline__ float row_ror(float x) {
-  return __int_as_float(row_ror<R>(__float_as_int(x)));
 }
 
 // Eight bf16 values (a 16-byte load) widened exactly to fp32.

@@ -36,11 +36,10 @@
 //          bf16 high part and a bf16 remainder so that p keeps 16 significant
 //          bits, never a single bf16 rounding; A = V^T read column-wise from the
 //          V rows in LDS.  For G = 1 (15 of 16 MFMA columns would repeat the
-//          head) on the vector ALUs in fp32: lane owns output dims
-//          8 col .. 8 col + 7 and tokens 4 qr + i; accumulator slot R holds query
-//          head gsel[R], the head of the lane that DPP row rotation R reaches,
-//          so that head's probabilities and rescale factors arrive by the same
-//          rotation.
+//          head) on the vector ALUs in fp32: lane (col, qr) owns output dims
+//          8 col .. 8 col + 7 of its tokens 4 qr + i, whose probabilities it
+//          already holds (every column is the one head), and the four row
+//          groups' sums are added at the end.
 //   loads  every K/V load instruction reads 4 whole 256-byte rows (lane
 //          (col, qr): 16 bytes of rows 4 qr + i); K reaches the A-operand
 //          layout of Q.K^T through a padded wave-private LDS tile.
@@ -56,78 +55,57 @@ namespace {
 constexpr int kD = 128;
 constexpr int kMaxWaves = 8;
 
-#if PKV_BALANCED_WAVES_PER_EU > 0
-#define PKV_BALANCED_OCCUPANCY \
-  __attribute__((amdgpu_waves_per_eu(PKV_BALANCED_WAVES_PER_EU, PKV_BALANCED_WAVES_PER_EU)))
-#else
-#define PKV_BALANCED_OCCUPANCY
-#endif
-
 // Eight E4M3 codes widened to eight bf16 values, exactly (an E4M3 value has
 // at most 4 significant bits); gfx950's conversions decode OCP E4M3.  The
-// scaled conversion with scale 1 gives two bf16 per instruction; the other
-// path goes through fp32 and keeps the top halves.
+// scaled conversion with scale 1 gives two bf16 per instruction.
 __device__ __forceinline__ u32x4_t widen_e4m3(u32x2_t w) {
   u32x4_t r;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-#if PKV_FP8_SCALED_CVT
     r[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[j], 1.f, false));
     r[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[j], 1.f, true));
-#else
-    const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], false);  // codes 4j, 4j + 1
-    const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], true);   // codes 4j + 2, 4j + 3
-    r[2 * j] = __builtin_amdgcn_perm(__float_as_uint(lo.y), __float_as_uint(lo.x), 0x07060302u);
-    r[2 * j + 1] = __builtin_amdgcn_perm(__float_as_uint(hi.y), __float_as_uint(hi.x), 0x07060302u);
-#endif
   }
   return r;
 }
 
-// K and V rows of one tile (TC chunks of 16 tokens) of one wave: for bf16
-// pools 16 bytes (8 elements) of each of 4 rows per lane; for FP8 pools 8
-// bytes (the same 8 elements) of each row and the K and V scales of the
-// rows' block.  krow/vrow give the rows as bf16.
-template <int TC, bool F8 = false>
+// K and V rows of one 16-token tile of one wave: for bf16 pools 16 bytes
+// (8 elements) of each of 4 rows per lane; for FP8 pools 8 bytes (the same
+// 8 elements) of each row and the K and V scales of the rows' block.
+// krow/vrow give the rows as bf16.
+template <bool F8 = false>
 struct KVTile;
 
-template <int TC>
-struct KVTile<TC, false> {
-  u32x4_t k[TC][4];
-  u32x4_t v[TC][4];
-  __device__ __forceinline__ u32x4_t krow(int c, int i) const { return k[c][i]; }
-  __device__ __forceinline__ u32x4_t vrow(int c, int i) const { return v[c][i]; }
+template <>
+struct KVTile<false> {
+  u32x4_t k[4];
+  u32x4_t v[4];
+  __device__ __forceinline__ u32x4_t krow(int i) const { return k[i]; }
+  __device__ __forceinline__ u32x4_t vrow(int i) const { return v[i]; }
   // An empty asm on every loaded register (see stream_window).
   __device__ __forceinline__ void pin() {
 #pragma unroll
-    for (int ch = 0; ch < TC; ++ch)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(k[ch][s]), "+v"(v[ch][s]));
+    for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(k[s]), "+v"(v[s]));
   }
 };
 
-template <int TC>
-struct KVTile<TC, true> {
-  u32x2_t k[TC][4];
-  u32x2_t v[TC][4];
-  float ks[TC], vs[TC];  // scales of the block of this lane's rows
-  __device__ __forceinline__ u32x4_t krow(int c, int i) const { return widen_e4m3(k[c][i]); }
-  __device__ __forceinline__ u32x4_t vrow(int c, int i) const { return widen_e4m3(v[c][i]); }
+template <>
+struct KVTile<true> {
+  u32x2_t k[4];
+  u32x2_t v[4];
+  float ks, vs;  // scales of the block of this lane's rows
+  __device__ __forceinline__ u32x4_t krow(int i) const { return widen_e4m3(k[i]); }
+  __device__ __forceinline__ u32x4_t vrow(int i) const { return widen_e4m3(v[i]); }
   __device__ __forceinline__ void pin() {
 #pragma unroll
-    for (int ch = 0; ch < TC; ++ch) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(k[ch][s]), "+v"(v[ch][s]));
-      asm volatile("" : "+v"(ks[ch]), "+v"(vs[ch]));
-    }
+    for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(k[s]), "+v"(v[s]));
+    asm volatile("" : "+v"(ks), "+v"(vs));
   }
 };
 
-// With PKV_K_VIA_LDS the K rows are loaded like the V rows (each load
-// instruction covers 4 whole 256-byte rows instead of 64 bytes of 16 rows)
-// and put into the MFMA operand layout through a wave-private LDS tile of
-// 16 rows, each padded to 17 x 16 bytes so that both the row writes and the
-// column reads are free of bank conflicts.
+// The K rows are loaded like the V rows (each load instruction covers 4
+// whole 256-byte rows) and put into the MFMA operand layout through a
+// wave-private LDS tile of 16 rows, each padded to 17 x 16 bytes so that
+// both the row writes and the column reads are free of bank conflicts.
 constexpr int kKRowPad = 17;  // 16-byte units per LDS row
 
 // The V tile of P.V on the matrix cores is read back with gfx950's
@@ -139,7 +117,7 @@ constexpr int kKRowPad = 17;  // 16-byte units per LDS row
 // one instruction (instead of four 16-bit reads).  Rows are padded to 18
 // 16-byte units, which puts the 8 rows a 32-lane half reads on 8 distinct
 // 8-bank groups.
-constexpr int kVRowPad = PKV_V_TR_READ ? 18 : kKRowPad;  // 16-byte units per V row
+constexpr int kVRowPad = 18;  // 16-byte units per V row
 
 __device__ __forceinline__ bf16x4_t lds_read_tr16(const uint16_t* p) {
   typedef short v4i16_t __attribute__((ext_vector_type(4)));
@@ -148,10 +126,8 @@ __device__ __forceinline__ bf16x4_t lds_read_tr16(const uint16_t* p) {
 }
 
 struct TileCtx {
-  const uint16_t* kbase;  // K pool + kv head offset + this lane's d-chunk (or dims)
+  const uint16_t* kbase;  // K pool + kv head offset + this lane's dims
   const uint16_t* vbase;  // V pool + kv head offset + this lane's dims
-  const uint16_t* kdead;  // this wave's query row + this lane's offset (see load_tile)
-  const uint16_t* vdead;  // this wave's query row + this lane's dims
   const uint8_t* kbase8;  // FP8 pools: K pool + kv head offset + this lane's dims
   const uint8_t* vbase8;  // FP8 pools: V pool + kv head offset + this lane's dims
   const float* kscale;    // FP8 pools: scales [num_blocks][num_kv_heads] + kv head
@@ -162,7 +138,7 @@ struct TileCtx {
   uint32_t row_bytes;     // bytes between consecutive slots
   uint32_t lane_bytes;    // this lane's byte offset inside a row (dims 8 col ..)
   uint32_t row_off[4];    // (4 qr + i) * row_bytes + lane_bytes: this lane's bytes of row i of a chunk
-  u32x4_t* k_lds;         // this wave's K transpose tile (PKV_K_VIA_LDS)
+  u32x4_t* k_lds;         // this wave's K transpose tile
   u32x4_t* v_lds;         // this wave's V tile, read column-wise (P.V on the matrix cores)
   int64_t tok_stride;     // elements between consecutive slots
   const int* s_bt;        // physical block ids of the window (LDS)
@@ -190,126 +166,84 @@ __device__ __forceinline__ void balance_issue(const TileCtx& c) {
 // 16 bytes of a K or V row; every K/V byte is read once per call, so the
 // loads may carry the streaming (non-temporal) hint.
 __device__ __forceinline__ u32x4_t load_kv(const uint16_t* p) {
-#if PKV_KV_NONTEMPORAL
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-#else
-  return *reinterpret_cast<const u32x4_t*>(p);
-#endif
 }
 
 // 8 bytes of an FP8 row, with the streaming hint like load_kv.
 __device__ __forceinline__ u32x2_t load_kv8(const uint8_t* p) {
-#if PKV_KV_NONTEMPORAL
   return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
-#else
-  return *reinterpret_cast<const u32x2_t*>(p);
-#endif
 }
 
-// Issue the loads of the tile starting at token t0.  Tokens past the end of
-// the window re-read its last token, so every address is a valid row (the
-// scores of such tokens are masked to -inf).  A chunk wholly past the end
-// (the prefetch after a window's last tile, never computed) reads this
-// wave's 256-byte query row instead, which is in cache, so it costs no HBM
-// traffic.  (Skipping those loads behind a wave-uniform branch instead makes
-// the compiler wait for all outstanding loads before the next tile's, which
-// undoes the prefetch.)  FP8 pools: a lane's 4 rows (4 qr .. 4 qr + 3,
-// clamped to the window's last token) always lie in one block, whose scales
-// it loads too; a dead chunk re-reads the last chunk (its codes must decode
-// to finite values: with several chunks per tile a dead chunk is computed,
-// and its values are multiplied by zero probabilities).
-template <int BS, int TC, bool F8 = false>
-__device__ __forceinline__ void load_tile(KVTile<TC, F8>& r, int t0, const TileCtx& c) {
+// Issue the loads of the 16-token tile starting at token t0.  Tokens past
+// the end of the window re-read its last token, so every address is a valid
+// row (the scores of such tokens are masked to -inf), and a tile wholly past
+// the end (the prefetch after a window's last tile, never computed) re-reads
+// the window's last chunk.  (Skipping those loads behind a wave-uniform
+// branch instead makes the compiler wait for all outstanding loads before
+// the next tile's, which undoes the prefetch.)  A lane's 4 rows
+// (4 qr .. 4 qr + 3, clamped to the window's last token) always lie in one
+// block, whose FP8 scales it loads too.
+template <int BS, bool F8 = false>
+__device__ __forceinline__ void load_tile(KVTile<F8>& r, int t0, const TileCtx& c) {
+  const int tce = min(t0, c.last_chunk);
+  if constexpr (BS >= 16) {
+    // The chunk lies in one block: its first row's address is wave-uniform
+    // (scalar registers) and a lane adds only the 32-bit offset of its row,
+    // row 4 qr + i clamped to the window's last token (tce is a multiple of
+    // 16, so tce + r stays in the block).
+    // min(r, lim) * row_bytes = min(r * row_bytes, lim * row_bytes).
+    const int phys = __builtin_amdgcn_readfirstlane(c.s_bt[tce / BS - c.blk0]);
+    const int tcu = __builtin_amdgcn_readfirstlane(tce);
+    const int lim = __builtin_amdgcn_readfirstlane(c.end - 1 - tcu);  // >= 0: tce <= last_chunk
+    const int64_t first = ((int64_t)phys * BS + (tcu & (BS - 1))) * c.row_bytes;
+    const uint8_t* kb = c.kpool + first;
+    const uint8_t* vb = c.vpool + first;
+    const uint32_t lim_off = (uint32_t)lim * c.row_bytes + c.lane_bytes;
 #pragma unroll
-  for (int ch = 0; ch < TC; ++ch) {
-    const bool dead = t0 + 16 * ch > c.last_chunk;
-    const int tce = min(t0 + 16 * ch, c.last_chunk);
-    const int tk = min(tce + c.col, c.end - 1);
-    int pk, pv[4];
-    if constexpr (BS >= 16) {
-      const int phys = __builtin_amdgcn_readfirstlane(c.s_bt[tce / BS - c.blk0]);
-      pk = phys;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pv[i] = phys;
-    } else {
-      pk = c.s_bt[tk / BS - c.blk0];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pv[i] = c.s_bt[min(tce + 4 * c.qr + i, c.end - 1) / BS - c.blk0];
-    }
-#if PKV_K_VIA_LDS
-    (void)pk;
-    if constexpr (BS >= 16 && PKV_SCALAR_BLOCK_BASE && (F8 || (TC == 1 && PKV_DEAD_REREAD))) {
-      // The chunk lies in one block: its first row's address is wave-uniform
-      // (scalar registers) and a lane adds only the 32-bit offset of its row,
-      // row 4 qr + i clamped to the window's last token, which is the same
-      // row as below (tce is a multiple of 16, so tce + r stays in the block).
-      // min(r, lim) * row_bytes = min(r * row_bytes, lim * row_bytes).
-      const int tcu = __builtin_amdgcn_readfirstlane(tce);
-      const int lim = __builtin_amdgcn_readfirstlane(c.end - 1 - tcu);  // >= 0: tce <= last_chunk
-      const int64_t first = ((int64_t)pk * BS + (tcu & (BS - 1))) * c.row_bytes;
-      const uint8_t* kb = c.kpool + first;
-      const uint8_t* vb = c.vpool + first;
-      const uint32_t lim_off = (uint32_t)lim * c.row_bytes + c.lane_bytes;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t off = min(c.row_off[i], lim_off);
-        if constexpr (F8) {
-          r.k[ch][i] = load_kv8(kb + off);
-          r.v[ch][i] = load_kv8(vb + off);
-        } else {
-          r.k[ch][i] = load_kv(reinterpret_cast<const uint16_t*>(kb + off));
-          r.v[ch][i] = load_kv(reinterpret_cast<const uint16_t*>(vb + off));
-        }
-      }
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t off = min(c.row_off[i], lim_off);
       if constexpr (F8) {
-        const int64_t si = (int64_t)pk * c.scale_stride;
-        r.ks[ch] = c.kscale[si];
-        r.vs[ch] = c.vscale[si];
+        r.k[i] = load_kv8(kb + off);
+        r.v[i] = load_kv8(vb + off);
+      } else {
+        r.k[i] = load_kv(reinterpret_cast<const uint16_t*>(kb + off));
+        r.v[i] = load_kv(reinterpret_cast<const uint16_t*>(vb + off));
       }
-      continue;
     }
+    if constexpr (F8) {
+      const int64_t si = (int64_t)phys * c.scale_stride;
+      r.ks = c.kscale[si];
+      r.vs = c.vscale[si];
+    }
+  } else {
+    // 8-token blocks: a chunk spans two blocks, each row finds its own.
+    int pv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {  // row 4 qr + i, dims 8 col .. 8 col + 7
       const int tv = min(tce + 4 * c.qr + i, c.end - 1);
+      pv[i] = c.s_bt[tv / BS - c.blk0];
       const int64_t row = ((int64_t)pv[i] * BS + (tv & (BS - 1))) * c.tok_stride;
       if constexpr (F8) {
-        r.k[ch][i] = load_kv8(c.kbase8 + row);
-        r.v[ch][i] = load_kv8(c.vbase8 + row);
-      } else if (TC == 1 && PKV_DEAD_REREAD) {
-        r.k[ch][i] = load_kv(c.kbase + row);
-        r.v[ch][i] = load_kv(c.vbase + row);
+        r.k[i] = load_kv8(c.kbase8 + row);
+        r.v[i] = load_kv8(c.vbase8 + row);
       } else {
-        r.k[ch][i] = load_kv(dead ? c.kdead : c.kbase + row);
-        r.v[ch][i] = load_kv(dead ? c.vdead : c.vbase + row);
+        r.k[i] = load_kv(c.kbase + row);
+        r.v[i] = load_kv(c.vbase + row);
       }
     }
     if constexpr (F8) {
       const int64_t si = (int64_t)pv[0] * c.scale_stride;
-      r.ks[ch] = c.kscale[si];
-      r.vs[ch] = c.vscale[si];
+      r.ks = c.kscale[si];
+      r.vs = c.vscale[si];
     }
-#else
-    static_assert(!F8, "FP8 pools load K rows like V rows");
-    const uint16_t* kp =
-        dead ? c.kdead : c.kbase + ((int64_t)pk * BS + (tk & (BS - 1))) * c.tok_stride;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) r.k[ch][s] = load_kv(kp + 32 * s);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tv = min(tce + 4 * c.qr + i, c.end - 1);
-      const uint16_t* vp =
-          dead ? c.vdead : c.vbase + ((int64_t)pv[i] * BS + (tv & (BS - 1))) * c.tok_stride;
-      r.v[ch][i] = load_kv(vp);
-    }
-#endif
   }
 }
 
-// P.V runs on the matrix cores for query groups of at least
-// PKV_PV_MFMA_MIN_GROUP heads; a single head would use one MFMA column in 16,
-// so it stays on the vector ALUs.
+// P.V runs on the matrix cores for query groups of at least 2 heads (p as
+// bf16 hi + lo); a single head would use one MFMA column in 16, so it stays
+// on the vector ALUs.
 template <int G>
-constexpr bool kPvOnMfma = G >= PKV_PV_MFMA_MIN_GROUP;
+constexpr bool kPvOnMfma = G >= 2;
 
 // Running softmax state of a wave whose P.V runs on the matrix cores, for NS
 // sets of 16 query columns; lane (col, qr) keeps column col of every set.
@@ -328,25 +262,22 @@ struct MfmaState {
   }
 };
 
-// Running softmax state of a wave whose P.V runs on the vector ALUs; one set
-// of columns, column col = query head col % G.
-template <int G>
+// Running softmax state of a wave whose P.V runs on the vector ALUs (a
+// single query head: every column holds it).
 struct ValuState {
-  float m[1], l[1];  // max and sum of head col % G (copies in every column with that head)
-  float acc[G][8];   // slot R: head gsel[R], dims 8 col .. 8 col + 7, this lane's token rows
+  float m[1], l[1];  // max and this lane's tokens' sum
+  float acc[8];      // dims 8 col .. 8 col + 7, this lane's token rows
   __device__ __forceinline__ void reset() {
     m[0] = -INFINITY;
     l[0] = 0.f;
 #pragma unroll
-    for (int r = 0; r < G; ++r)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
   }
 };
 
 // State of a wave over the G heads of its kv head (column col = head col % G).
 template <int G>
-using WaveState = std::conditional_t<kPvOnMfma<G>, MfmaState<1>, ValuState<G>>;
+using WaveState = std::conditional_t<kPvOnMfma<G>, MfmaState<1>, ValuState>;
 
 // Which tokens of a window a query column attends to.  WindowTokens: all of
 // them (decode).  CausalTokens: column set n of this lane stops below
@@ -399,17 +330,12 @@ __device__ __forceinline__ void scores_from_kop(const u32x4_t (&kop)[4], int c, 
 // first operand with row 2k of the second) and 32-lane halves without going
 // through LDS; the maximum of the two results is symmetric in the pair.
 __device__ __forceinline__ float rowgroup_max(float x) {
-#if PKV_PERMLANE_MAX
   const uint32_t u = __float_as_uint(x);
   const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
   const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const uint32_t v = __float_as_uint(y);
   const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-#else
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
-#endif
 }
 
 // Column maxima over the four row groups of a wave.
@@ -423,31 +349,23 @@ __device__ __forceinline__ void column_max(float (&mt)[NS]) {
 // scale * log2(e); tokens the columns do not attend to (at or past `end`, or
 // past a column's limit) score -inf.  mt[n] is the tile's maximum of set n
 // over each column (all four row groups).
-template <int TC, int NS, bool F8, class Lim = WindowTokens>
-__device__ __forceinline__ void tile_scores(const KVTile<TC, F8>& r, int t0, int end,
+template <int NS, bool F8, class Lim = WindowTokens>
+__device__ __forceinline__ void tile_scores(const KVTile<F8>& r, int t0, int end,
                                             const bf16x8_t (&qop)[NS][4], float scale_log2e,
-                                            const TileCtx& ctx, float (&x)[NS][TC][4],
+                                            const TileCtx& ctx, float (&x)[NS][1][4],
                                             float (&mt)[NS], const Lim& lim = Lim{}) {
   const int qr = ctx.qr;
 #pragma unroll
   for (int n = 0; n < NS; ++n) mt[n] = -INFINITY;
+  // rows as loaded -> LDS -> lane (col, qr) takes d-chunk 4 s + qr of row col
+  u32x4_t kop[4];
 #pragma unroll
-  for (int c = 0; c < TC; ++c) {
-    u32x4_t kop[4];
-#if PKV_K_VIA_LDS
-    // rows as loaded -> LDS -> lane (col, qr) takes d-chunk 4 s + qr of row col
+  for (int i = 0; i < 4; ++i) ctx.k_lds[(4 * qr + i) * kKRowPad + ctx.col] = r.krow(i);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ctx.k_lds[(4 * qr + i) * kKRowPad + ctx.col] = r.krow(c, i);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) kop[s] = ctx.k_lds[ctx.col * kKRowPad + 4 * s + qr];
-#else
-#pragma unroll
-    for (int s = 0; s < 4; ++s) kop[s] = r.krow(c, s);
-#endif
-    float sl = scale_log2e;
-    if constexpr (F8) sl *= r.ks[c];  // dequantised K = scale * code value
-    scores_from_kop<TC, NS>(kop, c, t0 + 16 * c, end, qop, sl, qr, x, mt, lim);
-  }
+  for (int s = 0; s < 4; ++s) kop[s] = ctx.k_lds[ctx.col * kKRowPad + 4 * s + qr];
+  float sl = scale_log2e;
+  if constexpr (F8) sl *= r.ks;  // dequantised K = scale * code value
+  scores_from_kop<1, NS>(kop, 0, t0, end, qop, sl, qr, x, mt, lim);
   column_max<NS>(mt);
 }
 
@@ -479,7 +397,7 @@ __device__ __forceinline__ void rescale_lazy(const float (&alpha)[NS], MfmaState
   bool moved = false;
 #pragma unroll
   for (int n = 0; n < NS; ++n) moved |= alpha[n] != 1.f;
-  if (!PKV_LAZY_RESCALE || __builtin_amdgcn_ballot_w64(moved) != 0) {
+  if (__builtin_amdgcn_ballot_w64(moved) != 0) {
 #pragma unroll
     for (int n = 0; n < NS; ++n)
 #pragma unroll
@@ -516,16 +434,8 @@ __device__ __forceinline__ void pv_from_lds(const uint16_t* vcol, int c,
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-#if PKV_V_TR_READ
     const bf16x4_t vt =
         lds_read_tr16(vcol + (4 * qr + col / 4) * (kVRowPad * 8) + 16 * j + 4 * (col % 4));
-#else
-    uint16_t e[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) e[t] = vcol[(4 * qr + t) * (kVRowPad * 8) + 16 * j + col];
-    const uint32_t va[2] = {e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16)};
-    const bf16x4_t vt = __builtin_bit_cast(bf16x4_t, va);
-#endif
 #pragma unroll
     for (int n = 0; n < NS; ++n) {
       st.o[n][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, phi[n], st.o[n][j], 0, 0, 0);
@@ -578,82 +488,50 @@ __device__ __forceinline__ void pv_pair_from_lds(const uint16_t* vcol0, const ui
 
 // Scores, online-softmax update and P.V accumulation for one loaded tile,
 // P.V on the matrix cores.
-template <int TC, int NS, bool F8, class Lim = WindowTokens>
-__device__ __forceinline__ void compute_tile(const KVTile<TC, F8>& r, int t0, int end,
+template <int NS, bool F8, class Lim = WindowTokens>
+__device__ __forceinline__ void compute_tile(const KVTile<F8>& r, int t0, int end,
                                              const bf16x8_t (&qop)[NS][4], float scale_log2e,
                                              const TileCtx& ctx, MfmaState<NS>& st,
                                              const Lim& lim = Lim{}) {
   const int qr = ctx.qr;
-  float x[NS][TC][4], mt[NS], alpha[NS];
-  tile_scores<TC, NS>(r, t0, end, qop, scale_log2e, ctx, x, mt, lim);
+  float x[NS][1][4], mt[NS], alpha[NS];
+  tile_scores<NS>(r, t0, end, qop, scale_log2e, ctx, x, mt, lim);
 #pragma unroll
-  for (int n = 0; n < NS; ++n) alpha[n] = softmax_update<TC>(x[n], mt[n], st.m[n], st.l[n]);
+  for (int n = 0; n < NS; ++n) alpha[n] = softmax_update<1>(x[n], mt[n], st.m[n], st.l[n]);
   if constexpr (F8) {  // dequantised V = scale * code value: scale the probabilities (not l)
 #pragma unroll
     for (int n = 0; n < NS; ++n)
 #pragma unroll
-      for (int c = 0; c < TC; ++c)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[n][c][i] *= r.vs[c];
+      for (int i = 0; i < 4; ++i) x[n][0][i] *= r.vs;
   }
   rescale_lazy<NS>(alpha, st);
-  const uint16_t* vcol = reinterpret_cast<const uint16_t*>(ctx.v_lds);
-  if constexpr (TC % 2 == 0 && PKV_PV_PAIRS) {
-    // all chunks' V rows to LDS (chunk c at rows 16 c ..), then P.V of
-    // chunk pairs with the 16x16x32 product
 #pragma unroll
-    for (int c = 0; c < TC; ++c)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        ctx.v_lds[(16 * c + 4 * qr + i) * kVRowPad + ctx.col] = r.vrow(c, i);
-#pragma unroll
-    for (int c = 0; c < TC; c += 2)
-      pv_pair_from_lds<TC, NS>(vcol + 16 * c * kVRowPad * 8, vcol + 16 * (c + 1) * kVRowPad * 8,
-                               c, c + 1, x, ctx.col, qr, st);
-  } else {
-#pragma unroll
-    for (int c = 0; c < TC; ++c) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ctx.v_lds[(4 * qr + i) * kVRowPad + ctx.col] = r.vrow(c, i);
-      pv_from_lds<TC, NS>(vcol, c, x, ctx.col, qr, st);
-    }
-  }
+  for (int i = 0; i < 4; ++i) ctx.v_lds[(4 * qr + i) * kVRowPad + ctx.col] = r.vrow(i);
+  pv_from_lds<1, NS>(reinterpret_cast<const uint16_t*>(ctx.v_lds), 0, x, ctx.col, qr, st);
 }
 
-// The same with P.V on the vector ALUs in fp32 (one column set, G heads).
-template <int TC, int G, bool F8>
-__device__ __forceinline__ void compute_tile(const KVTile<TC, F8>& r, int t0, int end,
+// The same with P.V on the vector ALUs in fp32 (one query head).
+template <bool F8>
+__device__ __forceinline__ void compute_tile(const KVTile<F8>& r, int t0, int end,
                                              const bf16x8_t (&qop)[1][4], float scale_log2e,
-                                             const TileCtx& ctx, ValuState<G>& st,
+                                             const TileCtx& ctx, ValuState& st,
                                              const WindowTokens& = WindowTokens{}) {
-  float x[1][TC][4], mt[1];
-  tile_scores<TC, 1>(r, t0, end, qop, scale_log2e, ctx, x, mt);
-  const float alpha = softmax_update<TC>(x[0], mt[0], st.m[0], st.l[0]);
-  if constexpr (F8) {  // each lane scales its own tokens' probabilities before they rotate
+  float x[1][1][4], mt[1];
+  tile_scores<1>(r, t0, end, qop, scale_log2e, ctx, x, mt);
+  const float alpha = softmax_update<1>(x[0], mt[0], st.m[0], st.l[0]);
+  if constexpr (F8) {  // dequantised V = scale * code value: scale the probabilities (not l)
 #pragma unroll
-    for (int c = 0; c < TC; ++c)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[0][c][i] *= r.vs[c];
+    for (int i = 0; i < 4; ++i) x[0][0][i] *= r.vs;
   }
-  static_for<G>([&](auto rr) {
-    constexpr int R = decltype(rr)::value;
-    const float ar = row_ror<R>(alpha);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) st.acc[R][e] *= ar;
-  });
+  for (int e = 0; e < 8; ++e) st.acc[e] *= alpha;
 #pragma unroll
-  for (int c = 0; c < TC; ++c)
+  for (int i = 0; i < 4; ++i) {
+    float vf[8];
+    unpack_bf16x8(r.vrow(i), vf);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float vf[8];
-      unpack_bf16x8(r.vrow(c, i), vf);
-      static_for<G>([&](auto rr) {
-        constexpr int R = decltype(rr)::value;
-        const float pr = row_ror<R>(x[0][c][i]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) st.acc[R][e] = fmaf(pr, vf[e], st.acc[R][e]);
-      });
-    }
+    for (int e = 0; e < 8; ++e) st.acc[e] = fmaf(x[0][0][i], vf[e], st.acc[e]);
+  }
 }
 
 // B operand of one set of query columns: this lane's column reads the
@@ -679,15 +557,15 @@ __device__ __forceinline__ void load_query(const DecodeArgs& a, int b, int kvh, 
 // loop-carried buffer the back edge copies the just-loaded registers, which
 // makes the wave wait for those loads at the end of every iteration.  The
 // scheduling barriers keep the loads ahead of the compute.  Past the window's
-// end the loads re-read its last chunk (or the query row) and are never used.
-template <int BS, int TC, bool F8, int NS, class State, class Lim = WindowTokens>
+// end the loads re-read its last chunk and are never used.
+template <int BS, bool F8, int NS, class State, class Lim = WindowTokens>
 __device__ __forceinline__ void stream_window(const DecodeArgs& a, const TileCtx& c, int begin,
                                               const bf16x8_t (&qop)[NS][4], State& st,
                                               const Lim& lim = Lim{}) {
-  constexpr int TILE = 16 * TC;
+  constexpr int TILE = 16;
   int t0 = begin;
-  KVTile<TC, F8> ta, tb;
-  load_tile<BS, TC>(ta, t0, c);
+  KVTile<F8> ta, tb;
+  load_tile<BS>(ta, t0, c);
   // The first tile passes through an empty asm so that ta is not a load on
   // both incoming edges of the loop: otherwise the optimiser merges the two
   // loads of ta into one at the loop top, which undoes the prefetch.
@@ -697,23 +575,21 @@ __device__ __forceinline__ void stream_window(const DecodeArgs& a, const TileCtx
   // head, and must then wait for every load at the head.
   const int n = (c.end - begin + TILE - 1) / TILE;  // tiles of the window (uniform)
   for (int i = 0; i + 1 < n; i += 2) {
-    load_tile<BS, TC>(tb, t0 + TILE, c);
+    load_tile<BS>(tb, t0 + TILE, c);
     __builtin_amdgcn_sched_barrier(0);
-    compute_tile<TC>(ta, t0, c.end, qop, a.scale_log2e, c, st, lim);
-    load_tile<BS, TC>(ta, t0 + 2 * TILE, c);
+    compute_tile(ta, t0, c.end, qop, a.scale_log2e, c, st, lim);
+    load_tile<BS>(ta, t0 + 2 * TILE, c);
     __builtin_amdgcn_sched_barrier(0);
-    compute_tile<TC>(tb, t0 + TILE, c.end, qop, a.scale_log2e, c, st, lim);
+    compute_tile(tb, t0 + TILE, c.end, qop, a.scale_log2e, c, st, lim);
     t0 += 2 * TILE;
     if (c.prog != nullptr) balance_issue(c);
   }
-  if (n & 1) compute_tile<TC>(ta, t0, c.end, qop, a.scale_log2e, c, st, lim);
-#if PKV_DRAIN_PREFETCH
+  if (n & 1) compute_tile(ta, t0, c.end, qop, a.scale_log2e, c, st, lim);
   // Wait here for the prefetch past the end (vmcnt 0; expcnt and lgkmcnt
   // left free).  Otherwise it is still in flight when the caller streams its
   // next window, whose loop head is the same code, and the compiler puts a
   // full wait at that head, in front of every other tile's loads.
   __builtin_amdgcn_s_waitcnt(0x0F70);
-#endif
 }
 
 // Sequences whose block tables must agree with the streamed table over every
@@ -727,14 +603,11 @@ struct TableCheck {
 // Streams tokens [begin, end) (begin a multiple of 16) through the block-table
 // row `bt` into the state of each wave, wave w for kv head kvh0 + w.  The
 // block ids of a window of up to kMaxPartitionTokens tokens go to LDS once for
-// all waves.  `qrow` is a 256-byte row of this wave's queries: the target of
-// the prefetch past the end, which is never used.  Every thread of the
-// workgroup calls this with the same range.
-template <int BS, int TC, bool kCheck, bool F8 = false, int NS, class State,
-          class Lim = WindowTokens>
+// all waves.  Every thread of the workgroup calls this with the same range.
+template <int BS, bool kCheck, bool F8 = false, int NS, class State, class Lim = WindowTokens>
 __device__ __forceinline__ void attend_table(const DecodeArgs& a, int* s_bt, u32x4_t* k_lds,
-                                             u32x4_t* v_lds, const int32_t* bt,
-                                             const uint16_t* qrow, int kvh, int begin, int end,
+                                             u32x4_t* v_lds, const int32_t* bt, int kvh,
+                                             int begin, int end,
                                              const bf16x8_t (&qop)[NS][4], State& st,
                                              TableCheck chk = TableCheck{nullptr, 0},
                                              const Lim& lim = Lim{}, int* prog = nullptr) {
@@ -745,17 +618,9 @@ __device__ __forceinline__ void attend_table(const DecodeArgs& a, int* s_bt, u32
   c.tok_stride = (int64_t)a.num_kv_heads * kD;
   c.col = lane & 15;
   c.qr = lane >> 4;
-#if PKV_K_VIA_LDS
   c.kbase = static_cast<const uint16_t*>(a.k_cache) + (int64_t)kvh * kD + 8 * c.col;
-  c.kdead = qrow + 8 * c.col;
   c.k_lds = k_lds;
-#else
-  c.kbase = static_cast<const uint16_t*>(a.k_cache) + (int64_t)kvh * kD + 8 * c.qr;
-  c.kdead = qrow + 8 * c.qr;  // + 32 s: 16 bytes inside the 128-element row
-  c.k_lds = nullptr;
-#endif
   c.vbase = static_cast<const uint16_t*>(a.v_cache) + (int64_t)kvh * kD + 8 * c.col;
-  c.vdead = qrow + 8 * c.col;
   c.v_lds = v_lds;
   c.s_bt = s_bt;
   {
@@ -795,21 +660,19 @@ __device__ __forceinline__ void attend_table(const DecodeArgs& a, int* s_bt, u32
     c.blk0 = blk0;
     c.end = wend;
     c.last_chunk = ((wend - 1) >> 4) << 4;
-    stream_window<BS, TC, F8>(a, c, w0, qop, st, lim);
+    stream_window<BS, F8>(a, c, w0, qop, st, lim);
   }
 }
 
 // attend_table over sequence b's own block table and queries.
-template <int G, int BS, int TC, bool F8 = false>
+template <int G, int BS, bool F8 = false>
 __device__ __forceinline__ void attend_range(const DecodeArgs& a, int* s_bt, u32x4_t* k_lds,
                                              u32x4_t* v_lds, int b, int kvh, int begin, int end,
                                              const bf16x8_t (&qop)[1][4], WaveState<G>& st,
                                              int* prog = nullptr) {
   const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
-  const uint16_t* qrow =
-      static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.num_q_heads + kvh * G) * kD;
-  attend_table<BS, TC, false, F8>(a, s_bt, k_lds, v_lds, bt, qrow, kvh, begin, end, qop, st,
-                                  TableCheck{nullptr, 0}, WindowTokens{}, prog);
+  attend_table<BS, false, F8>(a, s_bt, k_lds, v_lds, bt, kvh, begin, end, qop, st,
+                              TableCheck{nullptr, 0}, WindowTokens{}, prog);
 }
 
 // Where a wave's finished range goes.
@@ -853,42 +716,30 @@ __device__ __forceinline__ void finish_wave(const DecodeArgs& a, WaveState<G>& s
       }
     }
   } else {
+    // One query head (G = 1): add the four row groups' sums of the lane's
+    // dims; lanes of row group 0 write dims 8 col .. 8 col + 7.
 #pragma unroll
-    for (int r = 0; r < G; ++r)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        st.acc[r][e] += __shfl_xor(st.acc[r][e], 16);
-        st.acc[r][e] += __shfl_xor(st.acc[r][e], 32);
-      }
+    for (int e = 0; e < 8; ++e) {
+      st.acc[e] += __shfl_xor(st.acc[e], 16);
+      st.acc[e] += __shfl_xor(st.acc[e], 32);
+    }
     st.l[0] += __shfl_xor(st.l[0], 16);
     st.l[0] += __shfl_xor(st.l[0], 32);
-    // Head, max and sum of every slot, by the same rotation as the accumulation
-    // (computed by all lanes: DPP reads neighbouring lanes).
-    int hsel[G];
-    float msel[G], lsel[G];
-    static_for<G>([&](auto rr) {
-      constexpr int R = decltype(rr)::value;
-      hsel[R] = row_ror<R>(col % G);
-      msel[R] = row_ror<R>(st.m[0]);
-      lsel[R] = row_ror<R>(st.l[0]);
-    });
     if (qr != 0) return;
+    const int h = kvh * G;
+    if (sink.acc == nullptr) {
+      const int64_t o = ((int64_t)b * a.num_q_heads + h) * kD + 8 * col;
+      const float inv = 1.f / st.l[0];
 #pragma unroll
-    for (int r = 0; r < G; ++r) {
-      if (sink.acc == nullptr) {
-        const int64_t o = ((int64_t)b * a.num_q_heads + kvh * G + hsel[r]) * kD + 8 * col;
-        const float inv = 1.f / lsel[r];
+      for (int e = 0; e < 8; ++e) store_out(a, o + e, st.acc[e] * inv);
+    } else {
+      const int64_t row = sink.row0;
+      float* dst = sink.acc + row * kD + 8 * col;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) store_out(a, o + e, st.acc[r][e] * inv);
-      } else {
-        const int64_t row = sink.row0 + hsel[r] * sink.stride;
-        float* dst = sink.acc + row * kD + 8 * col;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dst[e] = st.acc[r][e];
-        if (col == 0) {
-          sink.max[row] = msel[r];
-          sink.sum[row] = lsel[r];
-        }
+      for (int e = 0; e < 8; ++e) dst[e] = st.acc[e];
+      if (col == 0) {
+        sink.max[row] = st.m[0];
+        sink.sum[row] = st.l[0];
       }
     }
   }

@@ -23,76 +23,18 @@ constexpr int kDefaultPartitionTokens = 512;
 constexpr int kMaxPartitionTokens = 4096;  // bounds the LDS window of block-table entries
 constexpr int kMaxBalancedSeqs = 2048;     // batch limit of the balanced schedule (LDS scan)
 
-// Build-time tuning of the bf16 decode kernels (defaults are the measured best).
-#ifndef PKV_MFMA_TILE_CHUNKS
-#define PKV_MFMA_TILE_CHUNKS 1  // 16-token chunks per wave tile
-#endif
-#ifndef PKV_FP8_TILE_CHUNKS
-#define PKV_FP8_TILE_CHUNKS 1  // the same for FP8 pools
-#endif
-#ifndef PKV_V_TR_READ
-#define PKV_V_TR_READ 1         // V^T operand of P.V read with ds_read_b64_tr_b16 (0: 16-bit reads)
-#endif
-#ifndef PKV_DEAD_REREAD
-#define PKV_DEAD_REREAD 1       // one chunk per tile: the prefetch past a window re-reads its last chunk
-#endif
-#ifndef PKV_DRAIN_PREFETCH
-#define PKV_DRAIN_PREFETCH 1    // drain the prefetch past a window's end before leaving it
-#endif
-#ifndef PKV_PV_PAIRS
-#define PKV_PV_PAIRS 1          // several chunks per tile: P.V of chunk pairs with the 16x16x32 product
-#endif
-#ifndef PKV_FP8_SCALED_CVT
-#define PKV_FP8_SCALED_CVT 1    // E4M3 -> bf16 with v_cvt_scalef32_pk_bf16_fp8 (0: via fp32 and a byte permute)
-#endif
-#ifndef PKV_PERMLANE_MAX
-#define PKV_PERMLANE_MAX 1      // column maxima across row groups with v_permlane{16,32}_swap (0: ds_bpermute)
-#endif
-#ifndef PKV_LAZY_RESCALE
-#define PKV_LAZY_RESCALE 1      // P.V accumulators rescaled only in tiles where a running max moved
-#endif
-#ifndef PKV_KV_NONTEMPORAL
-#define PKV_KV_NONTEMPORAL 1    // K/V loads carry the streaming hint (0: plain loads)
-#endif
-#ifndef PKV_SCALAR_BLOCK_BASE
-#define PKV_SCALAR_BLOCK_BASE 1 // block_size >= 16: a chunk's block address in scalar registers, 32-bit lane offsets
-#endif
-#ifndef PKV_K_VIA_LDS
-#define PKV_K_VIA_LDS 1         // K rows loaded 4 whole rows per instruction, transposed in LDS (0: MFMA layout loads)
-#endif
-#ifndef PKV_PV_MFMA_MIN_GROUP
-#define PKV_PV_MFMA_MIN_GROUP 2 // P.V on the matrix cores for query groups this large (p as bf16 hi + lo)
-#endif
-#ifndef PKV_BALANCED_WAVES_PER_EU
-#define PKV_BALANCED_WAVES_PER_EU 0  // > 0: ask the compiler for this occupancy (may spill)
-#endif
-#ifndef PKV_BALANCED_MAX_WAVES
-#define PKV_BALANCED_MAX_WAVES 8 // most waves (kv heads) per workgroup of the balanced schedule
-#endif
-#ifndef PKV_WAVE_BALANCE
-#define PKV_WAVE_BALANCE 1 // balanced schedule: issue priority to the wave behind its SIMD partner
-#endif
-#ifndef PKV_BALANCED_WGS
-#define PKV_BALANCED_WGS 256    // workgroups of the balanced schedule (all kv-head groups)
-#endif
-#ifndef PKV_SHARED_MIN_CHUNKS
-#define PKV_SHARED_MIN_CHUNKS 1 // shared-prefix schedule: fewest 16-token chunks per slice
-#endif
+// Workgroups of the balanced schedule over all kv-head groups: one per CU.
+constexpr int kBalancedWorkgroups = 256;
 
 // Waves per workgroup of the matrix-core kernels: one per kv head, the
 // largest of 8, 4, 2, 1 that divides num_kv_heads.
 int mfma_waves_per_group(int num_kv_heads);
 
-// Slices of the balanced schedule (per kv-head group).
-// Waves (kv heads) per workgroup of the balanced schedule.
-inline int balanced_waves_per_group(int num_kv_heads) {
-  const int kh = mfma_waves_per_group(num_kv_heads);
-  return kh < PKV_BALANCED_MAX_WAVES ? kh : PKV_BALANCED_MAX_WAVES;
-}
-
+// Slices of the balanced schedule per kv-head group (a workgroup's waves
+// cover one group of mfma_waves_per_group kv heads).
 inline int balanced_slices(int num_kv_heads) {
-  const int groups = num_kv_heads / balanced_waves_per_group(num_kv_heads);
-  return (PKV_BALANCED_WGS + groups - 1) / groups;
+  const int groups = num_kv_heads / mfma_waves_per_group(num_kv_heads);
+  return (kBalancedWorkgroups + groups - 1) / groups;
 }
 
 // Everything one decode launch needs; passed by value as a kernel argument.
@@ -200,7 +142,6 @@ struct SharedArgs {
   const int32_t* group_seqs;     //   group_seqs[group_offsets[g] .. group_offsets[g + 1])
   const int32_t* group_lens;     // [num_groups]: tokens every member maps to the same slots
   int32_t num_groups;
-  int32_t min_chunks;            // fewest 16-token chunks per slice
   int64_t prefix_rows;           // partial rows of prefix pieces; tail rows follow
 };
 
