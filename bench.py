@@ -59,6 +59,10 @@ def parse():
                    help="one line per workload (config 2, 4 at bs 32/64 with the balanced schedule "
                         "and with 512-token partitions, 5 at bs 8/16, FP8, prefill), then the "
                         "metric line")
+    p.add_argument("--only", default=None,
+                   help="only these --report-all lines, comma-separated: fp8, prefill, mha, "
+                        "long32, long32_p512, long64, long64_p512, swap, sharing4, sharing64 "
+                        "(for profiling one kernel's workload)")
     p.add_argument("--read-probe", action="store_true",
                    help="only time a plain streaming read of 4 GiB (context for the roofline)")
     p.add_argument("--copy-probe", action="store_true",
@@ -756,17 +760,25 @@ def with_baseline(res, args, fn, *a, gpu_key="attn_kv_gbps"):
     return res
 
 
-def report_all(torch, ops, args):
+def report_all(torch, ops, args, only=None):
     """One JSON line per workload other than the metric's (shorter runs), each
-    with the oracle timed beside it on the host."""
-    fp8_report(torch, ops, args)
-    prefill_report(torch, ops, args)
+    with the oracle timed beside it on the host; `only`: the names of the
+    lines to run (all when None)."""
+    want = lambda name: only is None or name in only  # noqa: E731
+    if want("fp8"):
+        fp8_report(torch, ops, args)
+    if want("prefill"):
+        prefill_report(torch, ops, args)
     from paged_kv_cache_330_amd.workloads import PrefixSharingWorkload, make_decode_workload
     steps, warmup = 20, 3
     # the Llama-7B MHA batch; the long-context batch at both block sizes, with
     # the balanced schedule and with its stated 512-token partitions (64 per
     # sequence, merged by the split-K reduce)
-    for config, bs, part in ((2, None, 0), (4, 32, 0), (4, 32, 512), (4, 64, 0), (4, 64, 512)):
+    for name, config, bs, part in (("mha", 2, None, 0), ("long32", 4, 32, 0),
+                                   ("long32_p512", 4, 32, 512), ("long64", 4, 64, 0),
+                                   ("long64_p512", 4, 64, 512)):
+        if not want(name):
+            continue
         w = make_decode_workload(config, block_size=bs)
         st = decode_step_state(torch, ops, w, args.pools, part)
         wall, t_copy, t_write, t_attn = time_steps(torch, st, steps, warmup)
@@ -780,7 +792,8 @@ def report_all(torch, ops, args):
         del st
         torch.cuda.empty_cache()
         print(json.dumps({"report": with_baseline(res, args, cpu_baseline, w)}), flush=True)
-    swap_report(torch, ops)
+    if want("swap"):
+        swap_report(torch, ops)
     # the prefix-sharing workload as stated (4 prompts x 8 samples) at both
     # block sizes, first divergent and last step; then 64 prompts x 8 samples
     # (512 sequences, 1.07 GB of unique K/V, 4.8 GB read by the plain decode),
@@ -788,6 +801,8 @@ def report_all(torch, ops, args):
     cases = [(4, bs, final) for bs in (8, 16) for final in (False, True)] + [(64, 16, True)]
     sharing_baselines = {}
     for prompts, bs, final in cases:
+        if not want(f"sharing{prompts}"):
+            continue
         kinds = [(False, False), (True, False)]
         if prompts == 64:
             kinds += [(False, True), (True, True)]
@@ -975,6 +990,9 @@ def main():
         return
     if args.fp8:
         fp8_report(torch, ops, args)
+        return
+    if args.only:
+        report_all(torch, ops, args, set(args.only.split(",")))
         return
     if args.report_all:
         report_all(torch, ops, args)

@@ -52,6 +52,20 @@ constexpr int kXcds = 8;  // XCDs of the device; workgroups go round-robin over 
 
 constexpr float kStaleMax = 8.f;  // log2 headroom of the running max
 
+// Sum of a lane's TC x 4 probabilities as a tree (a chain of adds would wait
+// on the adder's latency at every step).
+template <int TC>
+__device__ __forceinline__ float tile_sum(const float (&x)[TC][4]) {
+  float s[TC];
+#pragma unroll
+  for (int c = 0; c < TC; ++c) s[c] = (x[c][0] + x[c][1]) + (x[c][2] + x[c][3]);
+#pragma unroll
+  for (int w = 1; w < TC; w <<= 1)
+#pragma unroll
+    for (int c = 0; c + w < TC; c += 2 * w) s[c] += s[c + w];
+  return s[0];
+}
+
 // Online-softmax step of one column that moves the running max m only when
 // the tile's maximum exceeds it by more than 2^kStaleMax = 2^8.  Until
 // then the probabilities exp2(x - m) stay below 2^8
@@ -67,15 +81,11 @@ __device__ __forceinline__ float softmax_update_stale(float (&x)[TC][4], float m
   const float m_new = mt > m + kStaleMax ? mt : m;  // m = -inf: takes mt
   const float alpha = exp2_hw(m - m_new);
   m = m_new;
-  float psum = 0.f;
 #pragma unroll
   for (int c = 0; c < TC; ++c)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[c][i] = exp2_hw(x[c][i] - m_new);
-      psum += x[c][i];
-    }
-  l = l * alpha + psum;
+    for (int i = 0; i < 4; ++i) x[c][i] = exp2_hw(x[c][i] - m_new);
+  l = l * alpha + tile_sum<TC>(x);
   return alpha;
 }
 
@@ -90,15 +100,11 @@ __device__ __forceinline__ float softmax_update_stale_raw(float (&x)[TC][4], flo
   const float m_new = mts > m + kStaleMax ? mts : m;  // m = -inf: takes mts
   const float alpha = exp2_hw(m - m_new);
   m = m_new;
-  float psum = 0.f;
 #pragma unroll
   for (int c = 0; c < TC; ++c)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[c][i] = exp2_hw(fmaf(x[c][i], sl, -m_new));
-      psum += x[c][i];
-    }
-  l = l * alpha + psum;
+    for (int i = 0; i < 4; ++i) x[c][i] = exp2_hw(fmaf(x[c][i], sl, -m_new));
+  l = l * alpha + tile_sum<TC>(x);
   return alpha;
 }
 
@@ -298,23 +304,33 @@ __global__ __launch_bounds__(kItemThreads, 2) void prefill_kernel(PrefillArgs pa
       const u32x4_t* kt = s_k[buf];
       float x[kSharedSets][kTC][4], mt[kSharedSets], alpha[kSharedSets];
       __builtin_amdgcn_s_setprio(1);  // Q.K^T: this wave's products go first
+      {
+        // four independent accumulator chains (chunk, column set), k-step by
+        // k-step, so that consecutive products never wait on each other
+        u32x4_t kop[kTC][4];
 #pragma unroll
-      for (int c = 0; c < kTC; ++c) {
-        u32x4_t kop[4];
+        for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) kop[s] = kt[(16 * c + col) * kKRowPad + 4 * s + qr];
-        // FP8: the lane's 4 rows (4 qr ..) lie in one block; its K scale
-        // multiplies their scores
-        const float sl = F8 ? a.scale_log2e * s_ks[buf][16 * c + 4 * qr] : a.scale_log2e;
+          for (int c = 0; c < kTC; ++c) kop[c][s] = kt[(16 * c + col) * kKRowPad + 4 * s + qr];
+        f32x4_t sacc[kTC][kSharedSets];
 #pragma unroll
-        for (int m = 0; m < kSharedSets; ++m) {
-          f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < 4; ++s)
 #pragma unroll
-          for (int s = 0; s < 4; ++s)
-            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop[s]),
-                                                            qop[m][s], sacc, 0, 0, 0);
+          for (int c = 0; c < kTC; ++c)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) x[m][c][i] = kFold ? sacc[i] : sacc[i] * sl;
+            for (int m = 0; m < kSharedSets; ++m)
+              sacc[c][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8_t, kop[c][s]), qop[m][s],
+                  s == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : sacc[c][m], 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < kTC; ++c) {
+          // FP8: the lane's 4 rows (4 qr ..) lie in one block; its K scale
+          // multiplies their scores
+          const float sl = F8 ? a.scale_log2e * s_ks[buf][16 * c + 4 * qr] : a.scale_log2e;
+#pragma unroll
+          for (int m = 0; m < kSharedSets; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[m][c][i] = kFold ? sacc[c][m][i] : sacc[c][m][i] * sl;
         }
       }
       __builtin_amdgcn_s_setprio(0);  // softmax: the other wave's products may go first

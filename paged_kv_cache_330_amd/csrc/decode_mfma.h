@@ -473,17 +473,32 @@ __device__ __forceinline__ void pv_pair_from_lds(const uint16_t* vcol0, const ui
     plo[n] = __builtin_bit_cast(bf16x8_t, lo);
   }
   const int off = (4 * qr + col / 4) * (kVRowPad * 8) + 4 * (col % 4);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  auto read_v = [&](int j) {
     const bf16x4_t va = lds_read_tr16(vcol0 + off + 16 * j);
     const bf16x4_t vb = lds_read_tr16(vcol1 + off + 16 * j);
-    const bf16x8_t vt = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  // The high parts of 16-dim block j go in with the low parts of block
+  // j - 1, so that the two products on one accumulator are 2 NS products
+  // apart; the operand of block j + 1 is read meanwhile.
+  bf16x8_t vt[3];  // blocks j - 1, j, j + 1
+  vt[0] = read_v(0);
 #pragma unroll
-    for (int n = 0; n < NS; ++n) {
-      st.o[n][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, phi[n], st.o[n][j], 0, 0, 0);
-      st.o[n][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, plo[n], st.o[n][j], 0, 0, 0);
+  for (int j = 0; j < 8; ++j) {
+    if (j + 1 < 8) vt[(j + 1) % 3] = read_v(j + 1);
+#pragma unroll
+    for (int n = 0; n < NS; ++n)
+      st.o[n][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[j % 3], phi[n], st.o[n][j], 0, 0, 0);
+    if (j > 0) {
+#pragma unroll
+      for (int n = 0; n < NS; ++n)
+        st.o[n][j - 1] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[(j - 1) % 3], plo[n], st.o[n][j - 1], 0, 0, 0);
     }
   }
+#pragma unroll
+  for (int n = 0; n < NS; ++n)
+    st.o[n][7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[7 % 3], plo[n], st.o[n][7], 0, 0, 0);
 }
 
 // Scores, online-softmax update and P.V accumulation for one loaded tile,
