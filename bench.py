@@ -456,7 +456,12 @@ class Step:
     def decode_only(self, i):
         """The decode call of step i alone (no copies, no write)."""
         kc, vc = self.pools[i % len(self.pools)]
-        if self.fp8 is not None:
+        if self.fp8 is not None and self.groups is not None:
+            ks, vs = self.fp8
+            self.ops.pkv_attention_decode_shared_fp8(self.out, self.q, kc, vc, ks, vs, self.bt,
+                                                     self.sl, self.scale, *self.groups,
+                                                     workspace=self.ws)
+        elif self.fp8 is not None:
             ks, vs = self.fp8
             self.ops.pkv_attention_decode_fp8(self.out, self.q, kc, vc, ks, vs, self.bt, self.sl,
                                               self.scale, self.part, self.ws)
