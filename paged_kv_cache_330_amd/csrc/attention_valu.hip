@@ -164,6 +164,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a, int bloc
 // Split-K reduce of the partition grid: one workgroup per (query head,
 // sequence), one thread per output dimension:
 // out = sum_p e^(m_p - M) acc_p / sum_p e^(m_p - M) l_p,  M = max_p m_p.
+// Both loops are unrolled so that the loads of eight partitions are in
+// flight together (a long sequence has 64 partitions of 512 tokens).
 template <int D>
 __global__ __launch_bounds__(D) void splitk_reduce_kernel(DecodeArgs a, int block_size) {
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
@@ -171,12 +173,14 @@ __global__ __launch_bounds__(D) void splitk_reduce_kernel(DecodeArgs a, int bloc
   const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
   if (nparts <= 1) return;  // written by the main kernel
   const int64_t row = (int64_t)b * a.num_q_heads + h;
-  const float* mx = a.ws_max + row * a.max_parts;
-  const float* sm = a.ws_sum + row * a.max_parts;
-  const float* ac = a.ws_acc + row * a.max_parts * D;
+  const float* __restrict__ mx = a.ws_max + row * a.max_parts;
+  const float* __restrict__ sm = a.ws_sum + row * a.max_parts;
+  const float* __restrict__ ac = a.ws_acc + row * a.max_parts * D;
   float M = -INFINITY;
+#pragma unroll 8
   for (int p = 0; p < nparts; ++p) M = fmaxf(M, mx[p]);
   float num = 0.f, den = 0.f;
+#pragma unroll 8
   for (int p = 0; p < nparts; ++p) {
     const float sc = exp2_hw(mx[p] - M);
     num = fmaf(sc, ac[(int64_t)p * D + d], num);
