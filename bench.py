@@ -396,6 +396,37 @@ def cpu_baseline_sharing(prefix, bs, prompts, final, budget_s):
         tokens_per_s=round(passes * n / dt, 3))
 
 
+def cpu_baseline_swap(blocks, budget_s, chunk=64):
+    """The oracle's ``transfer_ref`` on the block-swap workload: a device-shaped
+    pool of 2 * ``blocks`` blocks and a host pool of ``blocks`` (bs 16, 8 kv
+    heads, head_dim 128, bf16 bit patterns, which a transfer moves unchanged).
+    A unit is ``chunk`` pairs swapped out and then back in; GB/s counts the K+V
+    bytes moved, both directions together, as the GPU figure ``swap_gbps``."""
+    import numpy as np
+    import oracle
+
+    rng = np.random.default_rng(11)
+    shape = (blocks * 2, 16, 8, 128)
+    kc = rng.integers(0, 1 << 16, size=shape, dtype=np.uint16)
+    vc = rng.integers(0, 1 << 16, size=shape, dtype=np.uint16)
+    hk = np.empty((blocks,) + shape[1:], dtype=np.uint16)
+    hv = np.empty_like(hk)
+    src = rng.permutation(blocks * 2)[:blocks]
+    pairs = np.stack([src, np.arange(blocks)], 1)
+    units = [pairs[i:i + chunk] for i in range(0, blocks, chunk)]
+
+    def one(u):
+        oracle.transfer_ref(hk, hv, kc, vc, u)
+        oracle.transfer_ref(kc, vc, hk, hv, u[:, ::-1])
+
+    n, passes, dt, threads, cores = _time_oracle(units, [len(u) for u in units], one, budget_s)
+    moved = passes * 2 * sum(len(u) for u in units[:n]) * 2 * 16 * 8 * 128 * 2
+    return _baseline_entry(
+        round(moved / dt / 1e9, 4), "GB/s", n, passes, dt, threads, cores,
+        (f"{passes} pass(es) of transfer_ref out and back in of {n} chunks of {chunk} "
+         f"blocks ({min(blocks, n * chunk)} of {blocks}), {threads} threads, {dt:.1f} s"))
+
+
 def cpu_baseline_prefill(w, budget_s, rows_wanted=4096):
     """The fp64 oracle on a bounded sample of prefill workload ``w``: a pass is
     ``write_ref`` of every prompt token, then ``prefill_ref`` of an evenly
@@ -720,7 +751,7 @@ def summary(name, extra, seq_lens, B, Hq, Hkv, D, bs, steps, wall, t_copy, t_wri
     return res, kv, alg
 
 
-def swap_report(torch, ops, blocks=2048, reps=5):
+def swap_report(torch, ops, args, blocks=2048, reps=5):
     """Swap 2048 blocks of the batch-256 GQA pool shape (bs 16, 8 kv heads,
     head_dim 128, bf16: 64 KiB of K+V per block) out to pinned host memory and
     back in, with pkv_block_transfer; GB/s of K+V moved each way."""
@@ -751,6 +782,8 @@ def swap_report(torch, ops, blocks=2048, reps=5):
         ms = statistics.median(ts)
         res[f"swap_{name}_us"] = round(ms * 1e3, 1)
         res[f"swap_{name}_gbps"] = round(nbytes / (ms * 1e-3) / 1e9, 2)
+    res["swap_gbps"] = round(2 * nbytes / ((res["swap_out_us"] + res["swap_in_us"]) * 1e-6) / 1e9, 2)
+    with_baseline(res, args, cpu_baseline_swap, blocks, gpu_key="swap_gbps")
     print(json.dumps({"report": res}), flush=True)
     del kc, vc, hk, hv
     torch.cuda.empty_cache()
@@ -798,7 +831,7 @@ def report_all(torch, ops, args, only=None):
         torch.cuda.empty_cache()
         print(json.dumps({"report": with_baseline(res, args, cpu_baseline, w)}), flush=True)
     if want("swap"):
-        swap_report(torch, ops)
+        swap_report(torch, ops, args)
     # the prefix-sharing workload as stated (4 prompts x 8 samples) at both
     # block sizes, first divergent and last step; then 64 prompts x 8 samples
     # (512 sequences, 1.07 GB of unique K/V, 4.8 GB read by the plain decode),

@@ -28,6 +28,12 @@ def test_sharing_and_prefill_baselines():
     check_entry(bench.cpu_baseline_prefill(pw, 0.2), "TFLOP/s")
 
 
+def test_swap_baseline():
+    e = bench.cpu_baseline_swap(128, 0.2, chunk=16)
+    check_entry(e, "GB/s")
+    assert "chunks of 16 blocks" in e["sample"]
+
+
 def test_algorithmic_bytes():
     # K/V rows + bf16 q + fp32 out + table entries + lengths
     kv, alg = bench.attn_bytes([16, 17], 2, 4, 2, 128, 16, 2)
