@@ -24,10 +24,11 @@
 // dense products of the K/V tile with 32 queries.  A tail stream covers one
 // sequence's own tokens with the G heads of its kv head, as in the plain
 // decode.  The 16-token chunks of all prefix streams, then of all tail
-// streams, are laid end to end and every workgroup takes an equal slice
-// (at least one chunk), as in the balanced schedule of the
-// plain decode.  Every workgroup derives the whole layout from the group
-// description and seq_lens in LDS.
+// streams, are laid end to end, each stream preceded by a few units that
+// stand for the start-up of its first piece, and every workgroup takes an
+// equal slice of that weighted stream (at least one unit), as in the balanced
+// schedule of the plain decode.  Every workgroup derives the whole layout
+// from the group description and seq_lens in LDS.
 //
 // Partial results.  A piece of stream st in slice s leaves its partial rows
 // at piece id st + s: consecutive streams never share a piece id, because the
@@ -54,6 +55,16 @@ template <int G>
 constexpr int kMembers = kCols / G;                          // sequences per prefix stream
 constexpr int kMaxPrefixStreams = kMaxBalancedSeqs + kMaxBalancedSeqs / kMembers<8>;
 constexpr int kMaxStreams = kMaxPrefixStreams + kMaxBalancedSeqs;
+// Start-up of a stream's first piece, in chunks, charged in the split: before
+// its first tile a prefix piece loads its members' queries and the lead's
+// table and checks the members' tables, a tail piece loads its table window
+// and queries.  Measured per piece, bf16 pools: prefix about 9 us and tail
+// about 2.5 us against 2.6 us per chunk streamed; FP8 pools stream a chunk in
+// about 1.5 us, so the same start-up is worth more chunks.
+template <bool F8>
+constexpr int kStartPrefix = F8 ? 8 : 5;
+template <bool F8>
+constexpr int kStartTail = F8 ? 2 : 1;
 
 // Writes the partial results of a prefix piece: stream column cw = 16 n + col
 // goes to row row0 + cw when cw < ncols (the columns of existing members).
@@ -92,6 +103,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_shared_kernel(SharedArg
   __shared__ int s_goff[kMaxBalancedSeqs + 1];  // member offsets of the groups
   __shared__ int s_gsp[kMaxBalancedSeqs + 1];   // first prefix stream of each group
   __shared__ int s_midx[kMaxBalancedSeqs];      // member index of each sequence, or -1
+  __shared__ int s_gseq[kMaxBalancedSeqs];      // the member list (group_seqs) as given
   __shared__ int s_tail[kMaxBalancedSeqs];      // first token of each sequence's tail
   __shared__ int s_len[kMaxBalancedSeqs];       // clamped length of each sequence
   __shared__ int s_glen[kMaxBalancedSeqs];      // shared length of each group as given
@@ -148,6 +160,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_shared_kernel(SharedArg
   // 2. Member index of every sequence (the last listing wins, deterministically).
   for (int i = threadIdx.x; i < M; i += blockDim.x) {
     const int seq = sa.group_seqs[i];
+    s_gseq[i] = seq;
     if (static_cast<unsigned>(seq) >= static_cast<unsigned>(B)) {
       if (reporter) atomicOr(a.err, kErrShared);
     } else if (atomicMax(&s_midx[seq], i) >= 0) {
@@ -174,33 +187,53 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_shared_kernel(SharedArg
   }
   __syncthreads();
 
-  // 5. Chunks of every stream: NPS prefix streams, then one tail per sequence.
+  // 5. The streams laid end to end: NPS prefix streams, then one tail per
+  //    sequence.  Each non-empty stream counts its chunks plus the start-up
+  //    its first piece costs, in chunks (kStartPrefix, kStartTail), so that a
+  //    slice that starts many streams gets fewer chunks (each slice also
+  //    continues one stream, so those start-ups even out).  s_cc holds these
+  //    weighted positions; stream st's chunk j sits at s_cc[st] + K(st) + j.
   const int NST = NPS + B;
-  const int total = block_scan(NST, s_cc, s_wsum, [&](int st) {
+  auto stream_chunks = [&](int st) {
     if (st < NPS) return prefix_tokens(last_at_most(s_gsp, NG, st)) >> 4;
     const int b = st - NPS;
     return s_len[b] > s_tail[b] ? (s_len[b] - s_tail[b] + 15) >> 4 : 0;
+  };
+  const int total = block_scan(NST, s_cc, s_wsum, [&](int st) {
+    const int n = stream_chunks(st);
+    return n > 0 ? n + (st < NPS ? kStartPrefix<F8> : kStartTail<F8>) : 0;
   });
   const int per = max(1, (total + S - 1) / S);
+  // start-up units and chunks of stream st, from its weighted span
+  auto span = [&](int st, int& k, int& n) {
+    const int w = s_cc[st + 1] - s_cc[st];
+    k = w > 0 ? (st < NPS ? kStartPrefix<F8> : kStartTail<F8>) : 0;
+    n = w - k;
+  };
 
   // 6. Merge descriptors, one workgroup: (merge needed, tail slices [tf, tl],
   //    prefix stream or -1, its slices [pf, pl], the member's first column).
+  //    A stream's pieces lie in the slices of its first and last chunks and
+  //    every slice between.
   if (blockIdx.x == 0 && slice == 0) {
     for (int b = threadIdx.x; b < B; b += blockDim.x) {
-      const int cs = s_cc[NPS + b], ce = s_cc[NPS + b + 1];
+      int k, n;
+      span(NPS + b, k, n);
       int tf = 0, tl = -1, pst = -1, pf = 0, pl = -1, cb = 0;
-      if (ce > cs) {
-        tf = cs / per;
-        tl = (ce - 1) / per;
+      if (n > 0) {
+        tf = (s_cc[NPS + b] + k) / per;
+        tl = (s_cc[NPS + b] + k + n - 1) / per;
       }
       if (s_tail[b] > 0) {
         const int i = s_midx[b];
         const int g = last_at_most(s_goff, NG, i);
-        const int k = i - s_goff[g];
-        pst = s_gsp[g] + k / MPS;
-        pf = s_cc[pst] / per;
-        pl = (s_cc[pst + 1] - 1) / per;
-        cb = (k % MPS) * G;
+        const int m = i - s_goff[g];
+        pst = s_gsp[g] + m / MPS;
+        int pk, pn;
+        span(pst, pk, pn);
+        pf = (s_cc[pst] + pk) / per;
+        pl = (s_cc[pst] + pk + pn - 1) / per;
+        cb = (m % MPS) * G;
       }
       int* d = a.ws_desc + kSharedDescInts * b;
       d[0] = (pst >= 0 || tl > tf) ? 1 : 0;
@@ -218,41 +251,46 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_shared_kernel(SharedArg
       return s_tail[j] == 0 && s_cc[NPS + j + 1] == s_cc[NPS + j];
     });
 
-  // 7. This slice's chunks.
-  const int c_lo = slice * per;
-  const int c_hi = min(total, c_lo + per);
-  if (c_lo >= c_hi) return;
+  // 7. This slice's part [x_lo, x_hi) of the weighted stream.
+  const int x_lo = slice * per;
+  const int x_hi = min(total, x_lo + per);
+  if (x_lo >= x_hi) return;
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
-  int st = last_at_most(s_cc, NST, c_lo);
-  int c = c_lo;
-  while (c < c_hi) {
-    while (s_cc[st + 1] <= c) ++st;  // skip streams with no chunks
-    const int cs = s_cc[st], ce = s_cc[st + 1];
-    const int c_end = min(c_hi, ce);
+  int st = last_at_most(s_cc, NST, x_lo);
+  int x = x_lo;
+  while (x < x_hi) {
+    while (s_cc[st + 1] <= x) ++st;  // skip empty streams and those ending at x
+    int k, n;
+    span(st, k, n);
+    const int w0 = s_cc[st] + k;               // weighted position of chunk 0
+    const int c0 = max(0, x - w0);             // this piece's chunks [c0, c1) of the stream
+    const int c1 = min(n, x_hi - w0);
+    x = min(x_hi, s_cc[st + 1]);
+    if (c1 <= c0) continue;                    // only the stream's start-up falls here
     if (st < NPS) {
       // Prefix piece: members m0 .. m0 + nm - 1 of group g, through m0's table.
       const int g = last_at_most(s_gsp, NG, st);
       const int m0 = s_goff[g] + (st - s_gsp[g]) * MPS;
       const int nm = min(MPS, s_goff[g + 1] - m0);
-      int lead = sa.group_seqs[m0];
+      int lead = s_gseq[m0];
       if (static_cast<unsigned>(lead) >= static_cast<unsigned>(B)) lead = 0;
       bf16x8_t qop[kSharedSets][4];
 #pragma unroll
-      for (int n = 0; n < kSharedSets; ++n) {
-        const int mi = (16 * n + col) / G;
-        int seq = mi < nm ? sa.group_seqs[m0 + mi] : lead;
+      for (int s2 = 0; s2 < kSharedSets; ++s2) {
+        const int mi = (16 * s2 + col) / G;
+        int seq = mi < nm ? s_gseq[m0 + mi] : lead;
         if (static_cast<unsigned>(seq) >= static_cast<unsigned>(B)) seq = lead;
-        load_qop(q + ((int64_t)seq * a.num_q_heads + kvh * G + col % G) * kD, qr, qop[n]);
+        load_qop(q + ((int64_t)seq * a.num_q_heads + kvh * G + col % G) * kD, qr, qop[s2]);
       }
       MfmaState<kSharedSets> ps;
       ps.reset();
       attend_table<BS, true, F8>(a, s_bt, k_lds, v_lds,
                                  a.block_tables + (int64_t)lead * a.max_blocks_per_seq, kvh,
-                                 (c - cs) * 16, (c_end - cs) * 16, qop, ps,
-                                 TableCheck{sa.group_seqs + m0, nm}, WindowTokens{}, prog);
+                                 c0 * 16, c1 * 16, qop, ps, TableCheck{s_gseq + m0, nm},
+                                 WindowTokens{}, prog);
       store_columns(a, ps, ((int64_t)(st + slice) * a.num_kv_heads + kvh) * kCols, nm * G);
     } else {
-      // Tail piece of sequence b: tokens T + 16 (c - cs) .. of its own table.
+      // Tail piece of sequence b: tokens T + 16 c0 .. of its own table.
       const int b = st - NPS;
       const int L = s_len[b];
       const int T = s_tail[b];
@@ -260,15 +298,14 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_shared_kernel(SharedArg
       load_query<G>(a, b, kvh, col, qr, qop);
       WaveState<G> ws;
       ws.reset();
-      attend_range<G, BS, F8>(a, s_bt, k_lds, v_lds, b, kvh, T + (c - cs) * 16,
-                                  min(T + (c_end - cs) * 16, L), qop, ws, prog);
+      attend_range<G, BS, F8>(a, s_bt, k_lds, v_lds, b, kvh, T + c0 * 16, min(T + c1 * 16, L),
+                              qop, ws, prog);
       Sink sink{nullptr, nullptr, nullptr, 0, 0};
-      if (!(T == 0 && c == cs && c_end == ce))
+      if (!(T == 0 && c0 == 0 && c1 == n))
         sink = Sink{a.ws_acc, a.ws_max, a.ws_sum,
                     sa.prefix_rows + ((int64_t)(b + slice) * a.num_kv_heads + kvh) * G, 1};
       finish_wave<G>(a, ws, b, kvh, sink);
     }
-    c = c_end;
   }
 }
 
