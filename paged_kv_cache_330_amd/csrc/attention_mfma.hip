@@ -7,8 +7,9 @@
 //    partition of part_tokens tokens), highest partition dispatched first;
 //    splitk_reduce_kernel merges the partitions of a sequence.
 //  * decode_balanced_kernel: the sequences' 16-token chunks are laid end to
-//    end and every workgroup takes an equal slice of that stream (see the
-//    kernel), so the work per workgroup does not depend on the length mix;
+//    end and every workgroup takes a slice of that stream (equal, up to the
+//    XCD-parity share; see the kernel), so the work per workgroup does not
+//    depend on the length mix;
 //    balanced_reduce_kernel merges the sequences that slices cut.
 #include "decode_mfma.h"
 
@@ -57,10 +58,11 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mfma_kernel(DecodeArgs 
 //
 // Every sequence is cut into 16-token chunks and the chunks of all sequences
 // are laid end to end (sequence 0's, then sequence 1's, ...).  For each
-// kv-head group, gridDim.y workgroups take equal consecutive slices of that
-// chunk stream, so every workgroup streams the same number of K/V bytes
-// whatever the length mix; a slice may cover the end of one sequence, several
-// whole sequences and the start of another.  Each workgroup computes the chunk
+// kv-head group, gridDim.y workgroups take consecutive slices of that chunk
+// stream of equal size (up to the XCD-parity share of SliceSplit), so every
+// workgroup streams about the same number of K/V bytes whatever the length
+// mix; a slice may cover the end of one sequence, several whole sequences and
+// the start of another.  Each workgroup computes the chunk
 // prefix sums of seq_lens in LDS.  A sequence that lies inside one slice is
 // written to `out` directly; a sequence cut by slice boundaries leaves one
 // partial (max, sum, unnormalised output) per piece and balanced_reduce_kernel
@@ -124,13 +126,13 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_balanced_kernel(DecodeA
   if (threadIdx.x == 0) s_cc[B] = carry;
   __syncthreads();
   const int total = s_cc[B];
-  const int per = max(1, (total + S - 1) / S);
+  const SliceSplit split = SliceSplit::make<F8>(total, S, gridDim.x);
 
   if (slice == 0)  // sequences of length 0 get zero rows
     zero_rows_where<G>(a, B, kvh, [&](int j) { return s_cc[j + 1] == s_cc[j]; });
 
-  const int c_lo = slice * per;
-  const int c_hi = min(total, c_lo + per);
+  const int c_lo = min(total, split.begin(slice));
+  const int c_hi = min(total, split.end(slice));
   if (c_lo >= c_hi) return;
   // first sequence of the slice: the largest b < B with s_cc[b] <= c_lo
   int lo = 0, hi = B;
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_balanced_kernel(DecodeA
     if (last && !first && blockIdx.x == 0 && threadIdx.x == 0) {
       // the final piece of a cut sequence: the reduce of this slice merges it
       desc[0] = b;
-      desc[1] = cb / per;  // slice of its first piece
+      desc[1] = split.slice_of(cb);  // slice of its first piece
     }
     c = c_end;
   }

@@ -25,9 +25,9 @@
 // sequence's own tokens with the G heads of its kv head, as in the plain
 // decode.  The 16-token chunks of all prefix streams, then of all tail
 // streams, are laid end to end, each stream preceded by a few units that
-// stand for the start-up of its first piece, and every workgroup takes an
-// equal slice of that weighted stream (at least one unit), as in the balanced
-// schedule of the plain decode.  Every workgroup derives the whole layout
+// stand for the start-up of its first piece, and every workgroup takes a
+// slice of that weighted stream (equal up to the XCD-parity share, at least
+// one unit), as in the balanced schedule of the plain decode.  Every workgroup derives the whole layout
 // from the group description and seq_lens in LDS.
 //
 // Partial results.  A piece of stream st in slice s leaves its partial rows
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_shared_kernel(SharedArg
     const int n = stream_chunks(st);
     return n > 0 ? n + (st < NPS ? kStartPrefix<F8> : kStartTail<F8>) : 0;
   });
-  const int per = max(1, (total + S - 1) / S);
+  const SliceSplit split = SliceSplit::make<F8>(total, S, gridDim.x);
   // start-up units and chunks of stream st, from its weighted span
   auto span = [&](int st, int& k, int& n) {
     const int w = s_cc[st + 1] - s_cc[st];
@@ -221,8 +221,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_shared_kernel(SharedArg
       span(NPS + b, k, n);
       int tf = 0, tl = -1, pst = -1, pf = 0, pl = -1, cb = 0;
       if (n > 0) {
-        tf = (s_cc[NPS + b] + k) / per;
-        tl = (s_cc[NPS + b] + k + n - 1) / per;
+        tf = split.slice_of(s_cc[NPS + b] + k);
+        tl = split.slice_of(s_cc[NPS + b] + k + n - 1);
       }
       if (s_tail[b] > 0) {
         const int i = s_midx[b];
@@ -231,8 +231,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_shared_kernel(SharedArg
         pst = s_gsp[g] + m / MPS;
         int pk, pn;
         span(pst, pk, pn);
-        pf = (s_cc[pst] + pk) / per;
-        pl = (s_cc[pst] + pk + pn - 1) / per;
+        pf = split.slice_of(s_cc[pst] + pk);
+        pl = split.slice_of(s_cc[pst] + pk + pn - 1);
         cb = (m % MPS) * G;
       }
       int* d = a.ws_desc + kSharedDescInts * b;
@@ -252,8 +252,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_shared_kernel(SharedArg
     });
 
   // 7. This slice's part [x_lo, x_hi) of the weighted stream.
-  const int x_lo = slice * per;
-  const int x_hi = min(total, x_lo + per);
+  const int x_lo = min(total, split.begin(slice));
+  const int x_hi = min(total, split.end(slice));
   if (x_lo >= x_hi) return;
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
   int st = last_at_most(s_cc, NST, x_lo);

@@ -690,6 +690,44 @@ __device__ __forceinline__ void attend_range(const DecodeArgs& a, int* s_bt, u32
                               TableCheck{nullptr, 0}, WindowTokens{}, prog);
 }
 
+// Slices of a work stream of `total` units, in pairs: slice 2k takes `even`
+// units of each pair's q, slice 2k + 1 the rest.  Workgroups are dealt
+// round-robin over the eight XCDs, so with one kv-head group per grid row
+// slice 2k runs on an even XCD and slice 2k + 1 on an odd one.  Timestamps of
+// the bf16 decode (a least-squares fit of each workgroup's time over its
+// chunks and pieces) leave a residual set by XCD parity alone: under a
+// full-bandwidth load the odd XCDs finish 17-24 us after the even ones over
+// about 250 us.  bf16 pools therefore give the even slice of a pair 51.5% of
+// its units; FP8 pools, which showed no such split, give both halves.  With an
+// even number of kv-head groups per row a slice's XCD parity is that of its
+// group, and with fewer than kXcdSplitMin units per slice (a small,
+// cache-resident call, where the share's rounding would outweigh it) the
+// slices stay equal.
+template <bool F8>
+constexpr int kXcdEvenPermille = F8 ? 500 : 515;
+constexpr int kXcdSplitMin = 48;
+
+struct SliceSplit {
+  int q;     // units per pair of slices
+  int even;  // units of its even slice
+  template <bool F8>
+  __device__ static SliceSplit make(int total, int slices, int groups) {
+    if (slices >= 2 && (groups & 1) && total >= kXcdSplitMin * slices) {
+      const int q = max(2, (total + slices / 2 - 1) / (slices / 2));
+      const int even = min(q - 1, max(1, (q * kXcdEvenPermille<F8> + 500) / 1000));
+      return {q, even};
+    }
+    const int per = max(1, (total + slices - 1) / slices);
+    return {2 * per, per};
+  }
+  __device__ int begin(int s) const { return (s >> 1) * q + ((s & 1) ? even : 0); }
+  __device__ int end(int s) const { return (s >> 1) * q + ((s & 1) ? q : even); }
+  __device__ int slice_of(int c) const {  // slice of unit c
+    const int p = c / q;
+    return 2 * p + (c - p * q >= even ? 1 : 0);
+  }
+};
+
 // Where a wave's finished range goes.
 struct Sink {
   float* acc;      // unnormalised output rows (D floats each), or nullptr: final output
