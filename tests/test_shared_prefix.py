@@ -19,8 +19,10 @@ import pytest
 torch = pytest.importorskip("torch")
 
 import oracle
+import oracle_threads
 from paged_kv_cache_330_amd.block_manager import BlockManager
-from paged_kv_cache_330_amd.workloads import bf16_round, torch_tensor
+from paged_kv_cache_330_amd.workloads import (PrefixSharingWorkload, bf16_round,
+                                              empty_device_caches, host_bits, torch_tensor)
 
 pytestmark = pytest.mark.gpu
 
@@ -237,6 +239,44 @@ def test_shared_decode_flags_inconsistent_descriptions(ops):
         if plain:
             assert_close(out.cpu().numpy(), batch.reference(), name)
     ops.pkv_check_device_errors()  # cleared
+
+
+def test_shared_decode_64_prompts_full_size(ops):
+    # The parallel-sampling workload scaled to 64 prompts x 8 samples (512
+    # sequences, 2044-token prompts, 256 generated tokens each): large enough
+    # that the slices are split by XCD parity and weighted by stream start-up.
+    # The pools are built step by step with the library's writes and
+    # copy-on-write copies, beside the oracle's, and must stay bit-identical;
+    # at the last step the shared-prefix decode is checked on every row.
+    dev = "cuda"
+    ws = PrefixSharingWorkload(prefix_len=2044, block_size=16, prompts=64)
+    say(f"  B={ws.num_seqs} blocks={ws.num_blocks}")
+    kc, vc = empty_device_caches(ws.num_blocks, 16, 8, D, "bf16", dev)
+    rk, rv = ws.empty_caches("nan")
+    pk, pv, ps = ws.prefill()
+    ops.pkv_kv_write(torch_tensor(pk, "bf16", dev), torch_tensor(pv, "bf16", dev),
+                     torch.from_numpy(ps).to(dev), kc, vc)
+    oracle.write_ref(pk, pv, ps, rk, rv)
+    for _ in range(ws.tail_len):
+        st = ws.next_step()
+        if len(st.copy_pairs):
+            ops.pkv_block_copy(kc, vc, torch.from_numpy(st.copy_pairs).to(dev))
+            oracle.copy_ref(rk, rv, st.copy_pairs)
+        ops.pkv_kv_write(torch_tensor(st.k_new, "bf16", dev), torch_tensor(st.v_new, "bf16", dev),
+                         torch.from_numpy(st.slot_mapping).to(dev), kc, vc)
+        oracle.write_ref(st.k_new, st.v_new, st.slot_mapping, rk, rv)
+    ops.pkv_check_device_errors()
+    assert np.array_equal(host_bits(kc).view(np.uint8), rk.view(np.uint8))
+    assert np.array_equal(host_bits(vc).view(np.uint8), rv.view(np.uint8))
+    groups = [torch.from_numpy(a).to(dev) for a in ws.manager.shared_prefix_groups(ws.seq_ids)]
+    out = torch.full((ws.num_seqs, 32, D), 7.0, dtype=torch.float32, device=dev)
+    ops.pkv_attention_decode_shared(out, torch_tensor(st.q, "bf16", dev), kc, vc,
+                                    torch.from_numpy(st.block_tables).to(dev),
+                                    torch.from_numpy(st.seq_lens).to(dev), float(ws.scale),
+                                    *groups)
+    ops.pkv_check_device_errors()
+    ref = oracle_threads.decode_rows(st.q, rk, rv, st.block_tables, st.seq_lens, ws.scale, "bf16")
+    assert_close(out.cpu().numpy(), ref, "64 x 8, step 256, every row")
 
 
 FP8_CASES = [c for c in CASES if c[0] in ("gqa4_bs16", "gqa4_bs8", "gqa4_members_7_9_17",
