@@ -241,16 +241,14 @@ def test_shared_decode_flags_inconsistent_descriptions(ops):
     ops.pkv_check_device_errors()  # cleared
 
 
-def test_shared_decode_64_prompts_full_size(ops):
-    # The parallel-sampling workload scaled to 64 prompts x 8 samples (512
-    # sequences, 2044-token prompts, 256 generated tokens each): large enough
-    # that the slices are split by XCD parity and weighted by stream start-up.
-    # The pools are built step by step with the library's writes and
-    # copy-on-write copies, beside the oracle's, and must stay bit-identical;
-    # at the last step the shared-prefix decode is checked on every row.
+@pytest.fixture(scope="module")
+def full64(ops):
+    """The parallel-sampling workload scaled to 64 prompts x 8 samples (512
+    sequences, 2044-token prompts, 256 generated tokens each), built step by
+    step with the library's writes and copy-on-write copies beside the
+    oracle's: (workload, last step, device pools, oracle pools, groups)."""
     dev = "cuda"
     ws = PrefixSharingWorkload(prefix_len=2044, block_size=16, prompts=64)
-    say(f"  B={ws.num_seqs} blocks={ws.num_blocks}")
     kc, vc = empty_device_caches(ws.num_blocks, 16, 8, D, "bf16", dev)
     rk, rv = ws.empty_caches("nan")
     pk, pv, ps = ws.prefill()
@@ -266,17 +264,66 @@ def test_shared_decode_64_prompts_full_size(ops):
                          torch.from_numpy(st.slot_mapping).to(dev), kc, vc)
         oracle.write_ref(st.k_new, st.v_new, st.slot_mapping, rk, rv)
     ops.pkv_check_device_errors()
+    groups = ws.manager.shared_prefix_groups(ws.seq_ids)
+    return ws, st, (kc, vc), (rk, rv), groups
+
+
+def test_shared_decode_64_prompts_full_size(ops, full64):
+    # Large enough that the slices are split by XCD parity and weighted by
+    # stream start-up.  The pools stay bit-identical to the oracle's after 256
+    # steps; the shared-prefix decode is checked on every row.
+    dev = "cuda"
+    ws, st, (kc, vc), (rk, rv), groups = full64
+    say(f"  B={ws.num_seqs} blocks={ws.num_blocks}")
     assert np.array_equal(host_bits(kc).view(np.uint8), rk.view(np.uint8))
     assert np.array_equal(host_bits(vc).view(np.uint8), rv.view(np.uint8))
-    groups = [torch.from_numpy(a).to(dev) for a in ws.manager.shared_prefix_groups(ws.seq_ids)]
+    g = [torch.from_numpy(a).to(dev) for a in groups]
     out = torch.full((ws.num_seqs, 32, D), 7.0, dtype=torch.float32, device=dev)
     ops.pkv_attention_decode_shared(out, torch_tensor(st.q, "bf16", dev), kc, vc,
                                     torch.from_numpy(st.block_tables).to(dev),
-                                    torch.from_numpy(st.seq_lens).to(dev), float(ws.scale),
-                                    *groups)
+                                    torch.from_numpy(st.seq_lens).to(dev), float(ws.scale), *g)
     ops.pkv_check_device_errors()
     ref = oracle_threads.decode_rows(st.q, rk, rv, st.block_tables, st.seq_lens, ws.scale, "bf16")
     assert_close(out.cpu().numpy(), ref, "64 x 8, step 256, every row")
+
+
+def test_shared_decode_64_prompts_full_size_fp8(ops, full64):
+    # The same pools' reached slots encoded into E4M3 pools (per-block scales
+    # from each block's own values, so the prompt blocks' scales are shared
+    # by all their sharers): codes bit-exact against the oracle's encoding,
+    # then the shared-prefix FP8 decode on every row against decode_ref over
+    # the dequantized pools.
+    from paged_kv_cache_330_amd.workloads import fp8_block_scales
+    dev = "cuda"
+    ws, st, _, (rk, rv), groups = full64
+    bs, nb = 16, ws.num_blocks
+    L = st.seq_lens.astype(np.int64)
+    reached = np.concatenate([st.block_tables[b, np.arange(L[b]) // bs].astype(np.int64) * bs
+                              + np.arange(L[b]) % bs for b in range(ws.num_seqs)])
+    slots = np.unique(reached)
+    flat = (nb * bs, 8, D)
+    kt, vt = rk.reshape(flat)[slots], rv.reshape(flat)[slots]
+    ks, vs = fp8_block_scales(kt, vt, slots, nb, bs, unused=1.0)
+    ck = np.full(rk.shape, 0x7F, np.uint8)
+    cv = ck.copy()
+    oracle_threads.write_fp8(kt, vt, slots, ck, cv, ks, vs)
+    kc8 = torch.full(rk.shape, 0x7F, dtype=torch.uint8, device=dev)
+    vc8 = kc8.clone()
+    tks, tvs = torch.from_numpy(ks).to(dev), torch.from_numpy(vs).to(dev)
+    ops.pkv_kv_write_fp8(torch_tensor(kt, "bf16", dev), torch_tensor(vt, "bf16", dev),
+                         torch.from_numpy(slots).to(dev), kc8, vc8, tks, tvs)
+    ops.pkv_check_device_errors()
+    assert np.array_equal(kc8.cpu().numpy(), ck) and np.array_equal(vc8.cpu().numpy(), cv)
+    g = [torch.from_numpy(a).to(dev) for a in groups]
+    out = torch.full((ws.num_seqs, 32, D), 7.0, dtype=torch.float32, device=dev)
+    ops.pkv_attention_decode_shared_fp8(out, torch_tensor(st.q, "bf16", dev), kc8, vc8, tks, tvs,
+                                        torch.from_numpy(st.block_tables).to(dev),
+                                        torch.from_numpy(st.seq_lens).to(dev), float(ws.scale),
+                                        *g)
+    ops.pkv_check_device_errors()
+    ref = oracle_threads.decode_fp8_rows(st.q, ck, cv, ks, vs, st.block_tables, st.seq_lens,
+                                         ws.scale)
+    assert_close(out.cpu().numpy(), ref, "FP8, 64 x 8, step 256, every row")
 
 
 FP8_CASES = [c for c in CASES if c[0] in ("gqa4_bs16", "gqa4_bs8", "gqa4_members_7_9_17",
