@@ -159,8 +159,8 @@ size_t pkv_attention_workspace_bytes(const pkv_cache_desc* cache, int32_t num_se
  *   scale         softmax scale applied to the fp32 dot products.
  *   partition_tokens  0 chooses the split: for bf16 pools with head_dim 128
  *                 and at most 2048 sequences, a balanced schedule that gives
- *                 every workgroup an equal share of all the sequences' tokens;
- *                 otherwise partitions of 512 tokens.  A positive value asks
+ *                 every workgroup about the same share of all the sequences'
+ *                 tokens; otherwise partitions of 512 tokens.  A positive value asks
  *                 for partitions of that many tokens: a multiple of 64 and of
  *                 block_size, at most 4096.
  *   workspace     pkv_attention_workspace_bytes(...) bytes of scratch (may be

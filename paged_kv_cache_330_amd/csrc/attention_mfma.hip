@@ -57,13 +57,15 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mfma_kernel(DecodeArgs 
 // Balanced schedule (up to kMaxBalancedSeqs sequences).
 //
 // Every sequence is cut into 16-token chunks and the chunks of all sequences
-// are laid end to end (sequence 0's, then sequence 1's, ...).  For each
-// kv-head group, gridDim.y workgroups take consecutive slices of that chunk
-// stream of equal size (up to the XCD-parity share of SliceSplit), so every
-// workgroup streams about the same number of K/V bytes whatever the length
-// mix; a slice may cover the end of one sequence, several whole sequences and
-// the start of another.  Each workgroup computes the chunk
-// prefix sums of seq_lens in LDS.  A sequence that lies inside one slice is
+// are laid end to end (sequence 0's, then sequence 1's, ...), each
+// sequence's chunks preceded by kStartSeq units that stand for the start of
+// its first piece.  For each kv-head group, gridDim.y workgroups take
+// consecutive slices of that weighted stream of equal size (up to the
+// XCD-parity share of SliceSplit), so every workgroup streams about the same
+// number of K/V bytes whatever the length mix; a slice may cover the end of
+// one sequence, several whole sequences and the start of another, or only a
+// sequence's start-up units.  Each workgroup computes the prefix sums of the
+// weighted counts in LDS.  A sequence that lies inside one slice is
 // written to `out` directly; a sequence cut by slice boundaries leaves one
 // partial (max, sum, unnormalised output) per piece and balanced_reduce_kernel
 // merges them.  Partial slot of a piece in slice s: 1 if the piece starts its
