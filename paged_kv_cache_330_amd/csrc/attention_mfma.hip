@@ -38,7 +38,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mfma_kernel(DecodeArgs 
     return;
   }
   const int lane = threadIdx.x & 63;
-  bf16x8_t qop[1][4];
+  QueryOperand<F8> qop[1];
   load_query<G>(a, b, kvh, lane & 15, lane >> 4, qop);
   WaveState<G> st;
   st.reset();
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_balanced_kernel(DecodeA
     const int tok_end = min(c1 * 16, L);
     const bool first = c0 == 0, last = c1 == n;
 
-    bf16x8_t qop[1][4];
+    QueryOperand<F8> qop[1];
     load_query<G>(a, b, kvh, lane & 15, lane >> 4, qop);
     WaveState<G> st;
     st.reset();

@@ -274,7 +274,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_shared_kernel(SharedArg
       const int nm = min(MPS, s_goff[g + 1] - m0);
       int lead = s_gseq[m0];
       if (static_cast<unsigned>(lead) >= static_cast<unsigned>(B)) lead = 0;
-      bf16x8_t qop[kSharedSets][4];
+      QueryOperand<F8> qop[kSharedSets];
 #pragma unroll
       for (int s2 = 0; s2 < kSharedSets; ++s2) {
         const int mi = (16 * s2 + col) / G;
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_shared_kernel(SharedArg
       const int b = st - NPS;
       const int L = s_len[b];
       const int T = s_tail[b];
-      bf16x8_t qop[1][4];
+      QueryOperand<F8> qop[1];
       load_query<G>(a, b, kvh, col, qr, qop);
       WaveState<G> ws;
       ws.reset();

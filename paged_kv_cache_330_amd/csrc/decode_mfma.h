@@ -43,6 +43,13 @@
 //   loads  every K/V load instruction reads 4 whole 256-byte rows (lane
 //          (col, qr): 16 bytes of rows 4 qr + i); K reaches the A-operand
 //          layout of Q.K^T through a padded wave-private LDS tile.
+// FP8 pools: lane (col, qr) loads the K codes of its A operand straight from
+// memory, bytes 16 qr .. 16 qr + 15 and 64 + 16 qr .. 64 + 16 qr + 15 of row
+// col (each of the two load instructions reads 64 contiguous bytes of all 16
+// rows), and widens them to bf16 in registers: no LDS tile for K.  The four
+// k-steps of Q.K^T take dims 64 (s / 2) + 8 (s % 2) + 16 qr .. + 7, and the
+// query operand follows that order.  V codes are widened to bf16 and P.V
+// runs as above.
 #pragma once
 
 #include <type_traits>
@@ -68,9 +75,20 @@ __device__ __forceinline__ u32x4_t widen_e4m3(u32x2_t w) {
   return r;
 }
 
+// Query operand of one set of 16 query columns; lane (col, qr) holds column
+// col: the B operands of the four 32-deep k-steps of Q.K^T, 8 bf16 each.
+// bf16 pools: dims 8 (4 s + qr) .. + 7 in step s (the K rows' order after
+// the LDS transpose); FP8 pools: dims 64 (s / 2) + 8 (s % 2) + 16 qr .. + 7
+// (the order in which a lane loads its K codes).
+template <bool F8>
+struct QueryOperand {
+  bf16x8_t s[4];
+};
+
 // K and V rows of one 16-token tile of one wave: for bf16 pools 16 bytes
 // (8 elements) of each of 4 rows per lane; for FP8 pools 8 bytes (the same
-// 8 elements) of each row and the K and V scales of the rows' block.
+// 8 elements) of each V row, the 32 K codes of the lane's operand of the
+// Q.K^T (row col), and the K and V scales of the block of rows 4 qr .. 4 qr + 3.
 // krow/vrow give the rows as bf16.
 template <bool F8 = false>
 struct KVTile;
@@ -90,15 +108,14 @@ struct KVTile<false> {
 
 template <>
 struct KVTile<true> {
-  u32x2_t k[4];
+  u32x4_t k[2];  // K codes of row col, dims 16 qr + j and 64 + 16 qr + j: the A operand of Q.K^T
   u32x2_t v[4];
-  float ks, vs;  // scales of the block of this lane's rows
-  __device__ __forceinline__ u32x4_t krow(int i) const { return widen_e4m3(k[i]); }
+  float ks, vs;  // scales of the block of this lane's rows 4 qr .. 4 qr + 3
   __device__ __forceinline__ u32x4_t vrow(int i) const { return widen_e4m3(v[i]); }
   __device__ __forceinline__ void pin() {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(k[s]), "+v"(v[s]));
-    asm volatile("" : "+v"(ks), "+v"(vs));
+    for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(v[s]));
+    asm volatile("" : "+v"(k[0]), "+v"(k[1]), "+v"(ks), "+v"(vs));
   }
 };
 
@@ -128,7 +145,6 @@ __device__ __forceinline__ bf16x4_t lds_read_tr16(const uint16_t* p) {
 struct TileCtx {
   const uint16_t* kbase;  // K pool + kv head offset + this lane's dims
   const uint16_t* vbase;  // V pool + kv head offset + this lane's dims
-  const uint8_t* kbase8;  // FP8 pools: K pool + kv head offset + this lane's dims
   const uint8_t* vbase8;  // FP8 pools: V pool + kv head offset + this lane's dims
   const float* kscale;    // FP8 pools: scales [num_blocks][num_kv_heads] + kv head
   const float* vscale;
@@ -138,6 +154,9 @@ struct TileCtx {
   uint32_t row_bytes;     // bytes between consecutive slots
   uint32_t lane_bytes;    // this lane's byte offset inside a row (dims 8 col ..)
   uint32_t row_off[4];    // (4 qr + i) * row_bytes + lane_bytes: this lane's bytes of row i of a chunk
+  uint32_t kcol_off;      // FP8 pools: col * row_bytes, the K row of this lane's Q.K^T operand
+  uint32_t kq_bytes;      // FP8 pools: 16 * qr, its first byte inside the row (and 64 more)
+  const uint8_t* kbase8q; // FP8 pools: K pool + kv head offset + kq_bytes
   u32x4_t* k_lds;         // this wave's K transpose tile
   u32x4_t* v_lds;         // this wave's V tile, read column-wise (P.V on the matrix cores)
   int64_t tok_stride;     // elements between consecutive slots
@@ -203,7 +222,6 @@ __device__ __forceinline__ void load_tile(KVTile<F8>& r, int t0, const TileCtx& 
     for (int i = 0; i < 4; ++i) {
       const uint32_t off = min(c.row_off[i], lim_off);
       if constexpr (F8) {
-        r.k[i] = load_kv8(kb + off);
         r.v[i] = load_kv8(vb + off);
       } else {
         r.k[i] = load_kv(reinterpret_cast<const uint16_t*>(kb + off));
@@ -211,6 +229,10 @@ __device__ __forceinline__ void load_tile(KVTile<F8>& r, int t0, const TileCtx& 
       }
     }
     if constexpr (F8) {
+      // K row col (clamped like the others), 32 codes in two 16-byte loads.
+      const uint32_t koff = min(c.kcol_off, (uint32_t)lim * c.row_bytes) + c.kq_bytes;
+      r.k[0] = load_kv(reinterpret_cast<const uint16_t*>(kb + koff));
+      r.k[1] = load_kv(reinterpret_cast<const uint16_t*>(kb + koff + 64));
       const int64_t si = (int64_t)phys * c.scale_stride;
       r.ks = c.kscale[si];
       r.vs = c.vscale[si];
@@ -224,7 +246,6 @@ __device__ __forceinline__ void load_tile(KVTile<F8>& r, int t0, const TileCtx& 
       pv[i] = c.s_bt[tv / BS - c.blk0];
       const int64_t row = ((int64_t)pv[i] * BS + (tv & (BS - 1))) * c.tok_stride;
       if constexpr (F8) {
-        r.k[i] = load_kv8(c.kbase8 + row);
         r.v[i] = load_kv8(c.vbase8 + row);
       } else {
         r.k[i] = load_kv(c.kbase + row);
@@ -232,6 +253,13 @@ __device__ __forceinline__ void load_tile(KVTile<F8>& r, int t0, const TileCtx& 
       }
     }
     if constexpr (F8) {
+      // K row col of the chunk (the Q.K^T operand), in its own block.
+      const int tk = min(tce + c.col, c.end - 1);
+      const int pk = c.s_bt[tk / BS - c.blk0];
+      const uint16_t* kp = reinterpret_cast<const uint16_t*>(
+          c.kbase8q + ((int64_t)pk * BS + (tk & (BS - 1))) * c.tok_stride);
+      r.k[0] = load_kv(kp);
+      r.k[1] = load_kv(kp + 32);
       const int64_t si = (int64_t)pv[0] * c.scale_stride;
       r.ks = c.kscale[si];
       r.vs = c.vscale[si];
@@ -297,31 +325,25 @@ struct CausalTokens {
   __device__ __forceinline__ bool whole(int, int) const { return false; }
 };
 
-// Q.K^T of chunk c (tokens tok0 .. tok0 + 15) for NS sets of query columns
-// from the chunk's K operand (lane (col, qr): d-chunk 4 s + qr of row col),
-// scaled by sl; tokens a column does not attend to score -inf.  mt[n] takes
-// the maximum of set n over this lane's rows.
-template <int TC, int NS, class Lim>
-__device__ __forceinline__ void scores_from_kop(const u32x4_t (&kop)[4], int c, int tok0, int end,
-                                                const bf16x8_t (&qop)[NS][4], float sl, int qr,
-                                                float (&x)[NS][TC][4], float (&mt)[NS],
-                                                const Lim& lim) {
+// Scores of one chunk (tokens tok0 .. tok0 + 15) from the raw products
+// sacc of NS sets of query columns times sl[n]; tokens a column does not
+// attend to score -inf.  mt[n] takes the maximum of set n over this lane's
+// rows (lane (col, qr), register i: token 4 qr + i).
+template <int NS, class Lim>
+__device__ __forceinline__ void scores_of_chunk(const f32x4_t (&sacc)[NS], const float (&sl)[NS],
+                                                int tok0, int end, int qr, float (&x)[NS][1][4],
+                                                float (&mt)[NS], const Lim& lim) {
 #pragma unroll
   for (int n = 0; n < NS; ++n) {
-    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop[s]),
-                                                      qop[n][s], sacc, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[n][c][i] = sacc[i] * sl;
+    for (int i = 0; i < 4; ++i) x[n][0][i] = sacc[n][i] * sl[n];
     if (!lim.whole(tok0, end)) {  // only a window's last chunk holds tokens past its end
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (!lim.valid(n, tok0 + 4 * qr + i, end)) x[n][c][i] = -INFINITY;
+        if (!lim.valid(n, tok0 + 4 * qr + i, end)) x[n][0][i] = -INFINITY;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) mt[n] = fmaxf(mt[n], x[n][c][i]);
+    for (int i = 0; i < 4; ++i) mt[n] = fmaxf(mt[n], x[n][0][i]);
   }
 }
 
@@ -351,21 +373,49 @@ __device__ __forceinline__ void column_max(float (&mt)[NS]) {
 // over each column (all four row groups).
 template <int NS, bool F8, class Lim = WindowTokens>
 __device__ __forceinline__ void tile_scores(const KVTile<F8>& r, int t0, int end,
-                                            const bf16x8_t (&qop)[NS][4], float scale_log2e,
+                                            const QueryOperand<F8> (&qop)[NS], float scale_log2e,
                                             const TileCtx& ctx, float (&x)[NS][1][4],
                                             float (&mt)[NS], const Lim& lim = Lim{}) {
   const int qr = ctx.qr;
+  f32x4_t sacc[NS];
+  float sl[NS];
 #pragma unroll
-  for (int n = 0; n < NS; ++n) mt[n] = -INFINITY;
-  // rows as loaded -> LDS -> lane (col, qr) takes d-chunk 4 s + qr of row col
-  u32x4_t kop[4];
+  for (int n = 0; n < NS; ++n) {
+    mt[n] = -INFINITY;
+    sacc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  if constexpr (F8) {
+    // A = the K codes as loaded, widened (exactly) to bf16: k-step s takes
+    // codes 8 s .. 8 s + 7 of this lane.  Dequantised K = scale * code value.
+    u32x4_t kop[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) ctx.k_lds[(4 * qr + i) * kKRowPad + ctx.col] = r.krow(i);
+    for (int s = 0; s < 4; ++s)
+      kop[s] = widen_e4m3(u32x2_t{r.k[s >> 1][2 * (s & 1)], r.k[s >> 1][2 * (s & 1) + 1]});
 #pragma unroll
-  for (int s = 0; s < 4; ++s) kop[s] = ctx.k_lds[ctx.col * kKRowPad + 4 * s + qr];
-  float sl = scale_log2e;
-  if constexpr (F8) sl *= r.ks;  // dequantised K = scale * code value
-  scores_from_kop<1, NS>(kop, 0, t0, end, qop, sl, qr, x, mt, lim);
+    for (int n = 0; n < NS; ++n) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        sacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop[s]),
+                                                          qop[n].s[s], sacc[n], 0, 0, 0);
+      sl[n] = scale_log2e * r.ks;
+    }
+  } else {
+    // rows as loaded -> LDS -> lane (col, qr) takes d-chunk 4 s + qr of row col
+    u32x4_t kop[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ctx.k_lds[(4 * qr + i) * kKRowPad + ctx.col] = r.krow(i);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) kop[s] = ctx.k_lds[ctx.col * kKRowPad + 4 * s + qr];
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        sacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop[s]),
+                                                          qop[n].s[s], sacc[n], 0, 0, 0);
+      sl[n] = scale_log2e;
+    }
+  }
+  scores_of_chunk<NS>(sacc, sl, t0, end, qr, x, mt, lim);
   column_max<NS>(mt);
 }
 
@@ -505,7 +555,7 @@ __device__ __forceinline__ void pv_pair_from_lds(const uint16_t* vcol0, const ui
 // P.V on the matrix cores.
 template <int NS, bool F8, class Lim = WindowTokens>
 __device__ __forceinline__ void compute_tile(const KVTile<F8>& r, int t0, int end,
-                                             const bf16x8_t (&qop)[NS][4], float scale_log2e,
+                                             const QueryOperand<F8> (&qop)[NS], float scale_log2e,
                                              const TileCtx& ctx, MfmaState<NS>& st,
                                              const Lim& lim = Lim{}) {
   const int qr = ctx.qr;
@@ -528,7 +578,7 @@ __device__ __forceinline__ void compute_tile(const KVTile<F8>& r, int t0, int en
 // The same with P.V on the vector ALUs in fp32 (one query head).
 template <bool F8>
 __device__ __forceinline__ void compute_tile(const KVTile<F8>& r, int t0, int end,
-                                             const bf16x8_t (&qop)[1][4], float scale_log2e,
+                                             const QueryOperand<F8> (&qop)[1], float scale_log2e,
                                              const TileCtx& ctx, ValuState& st,
                                              const WindowTokens& = WindowTokens{}) {
   float x[1][1][4], mt[1];
@@ -557,10 +607,22 @@ __device__ __forceinline__ void load_qop(const uint16_t* qrow, int qr, bf16x8_t 
     qop[s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * qr));
 }
 
+__device__ __forceinline__ void load_qop(const uint16_t* qrow, int qr, QueryOperand<false>& op) {
+  load_qop(qrow, qr, op.s);
+}
+
+// The FP8 pools' order: k-step s reads dims 64 (s / 2) + 8 (s % 2) + 16 qr .. + 7.
+__device__ __forceinline__ void load_qop(const uint16_t* qrow, int qr, QueryOperand<true>& op) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    op.s[s] = __builtin_bit_cast(
+        bf16x8_t, *reinterpret_cast<const uint4*>(qrow + 64 * (s >> 1) + 8 * (s & 1) + 16 * qr));
+}
+
 // Query operand of the group of kv head kvh, sequence b (column col = head col % G).
-template <int G>
+template <int G, bool F8>
 __device__ __forceinline__ void load_query(const DecodeArgs& a, int b, int kvh, int col, int qr,
-                                           bf16x8_t (&qop)[1][4]) {
+                                           QueryOperand<F8> (&qop)[1]) {
   load_qop(static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.num_q_heads + kvh * G + col % G) * kD,
            qr, qop[0]);
 }
@@ -575,7 +637,7 @@ __device__ __forceinline__ void load_query(const DecodeArgs& a, int b, int kvh, 
 // end the loads re-read its last chunk and are never used.
 template <int BS, bool F8, int NS, class State, class Lim = WindowTokens>
 __device__ __forceinline__ void stream_window(const DecodeArgs& a, const TileCtx& c, int begin,
-                                              const bf16x8_t (&qop)[NS][4], State& st,
+                                              const QueryOperand<F8> (&qop)[NS], State& st,
                                               const Lim& lim = Lim{}) {
   constexpr int TILE = 16;
   int t0 = begin;
@@ -623,7 +685,7 @@ template <int BS, bool kCheck, bool F8 = false, int NS, class State, class Lim =
 __device__ __forceinline__ void attend_table(const DecodeArgs& a, int* s_bt, u32x4_t* k_lds,
                                              u32x4_t* v_lds, const int32_t* bt, int kvh,
                                              int begin, int end,
-                                             const bf16x8_t (&qop)[NS][4], State& st,
+                                             const QueryOperand<F8> (&qop)[NS], State& st,
                                              TableCheck chk = TableCheck{nullptr, 0},
                                              const Lim& lim = Lim{}, int* prog = nullptr) {
   const int lane = threadIdx.x & 63;
@@ -648,7 +710,9 @@ __device__ __forceinline__ void attend_table(const DecodeArgs& a, int* s_bt, u32
     for (int i = 0; i < 4; ++i) c.row_off[i] = (uint32_t)(4 * c.qr + i) * c.row_bytes + c.lane_bytes;
   }
   if constexpr (F8) {
-    c.kbase8 = static_cast<const uint8_t*>(a.k_cache) + (int64_t)kvh * kD + 8 * c.col;
+    c.kcol_off = (uint32_t)c.col * c.row_bytes;
+    c.kq_bytes = 16u * c.qr;
+    c.kbase8q = static_cast<const uint8_t*>(a.k_cache) + (int64_t)kvh * kD + c.kq_bytes;
     c.vbase8 = static_cast<const uint8_t*>(a.v_cache) + (int64_t)kvh * kD + 8 * c.col;
     c.kscale = a.k_scale + kvh;
     c.vscale = a.v_scale + kvh;
@@ -683,7 +747,7 @@ __device__ __forceinline__ void attend_table(const DecodeArgs& a, int* s_bt, u32
 template <int G, int BS, bool F8 = false>
 __device__ __forceinline__ void attend_range(const DecodeArgs& a, int* s_bt, u32x4_t* k_lds,
                                              u32x4_t* v_lds, int b, int kvh, int begin, int end,
-                                             const bf16x8_t (&qop)[1][4], WaveState<G>& st,
+                                             const QueryOperand<F8> (&qop)[1], WaveState<G>& st,
                                              int* prog = nullptr) {
   const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
   attend_table<BS, false, F8>(a, s_bt, k_lds, v_lds, bt, kvh, begin, end, qop, st,
