@@ -44,7 +44,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--config", type=int, default=3)
     p.add_argument("--block-size", type=int, default=None)
     p.add_argument("--partition-tokens", type=int, default=0)
