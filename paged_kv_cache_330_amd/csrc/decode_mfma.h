@@ -119,9 +119,9 @@ struct KVTile<true> {
   }
 };
 
-// The K rows are loaded like the V rows (each load instruction covers 4
-// whole 256-byte rows) and put into the MFMA operand layout through a
-// wave-private LDS tile of 16 rows, each padded to 17 x 16 bytes so that
+// bf16 pools: the K rows are loaded like the V rows (each load instruction
+// covers 4 whole 256-byte rows) and put into the MFMA operand layout through
+// a wave-private LDS tile of 16 rows, each padded to 17 x 16 bytes so that
 // both the row writes and the column reads are free of bank conflicts.
 constexpr int kKRowPad = 17;  // 16-byte units per LDS row
 
@@ -157,7 +157,7 @@ struct TileCtx {
   uint32_t kcol_off;      // FP8 pools: col * row_bytes, the K row of this lane's Q.K^T operand
   uint32_t kq_bytes;      // FP8 pools: 16 * qr, its first byte inside the row (and 64 more)
   const uint8_t* kbase8q; // FP8 pools: K pool + kv head offset + kq_bytes
-  u32x4_t* k_lds;         // this wave's K transpose tile
+  u32x4_t* k_lds;         // this wave's K transpose tile (bf16 pools)
   u32x4_t* v_lds;         // this wave's V tile, read column-wise (P.V on the matrix cores)
   int64_t tok_stride;     // elements between consecutive slots
   const int* s_bt;        // physical block ids of the window (LDS)
