@@ -228,6 +228,9 @@ CASES = [
     ("gqa8_bs64_outliers", 4, (64, 65, 1030), 64, None),
     ("gqa2_bs16", 3, (3, 77, 520), 16, (16, 8)),
     ("hkv4_gqa4_bs8", 3, (5, 70, 600), 8, (16, 4)),
+    ("gqa4_hkv6", 3, (3, 200, 1100, 17), 16, (24, 6)),
+    ("gqa2_hkv5_bs8", 3, (17, 500, 1, 64), 8, (10, 5)),
+    ("mha_hkv3", 2, (33, 900, 2), 16, (3, 3)),
 ]
 
 

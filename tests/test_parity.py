@@ -113,6 +113,13 @@ SMALL_CASES = [
     ("bf16_d64_gqa4", 3, (5, 70, 600), 16, (16, 4), 64, None),
     ("f32_d128_gqa8", 3, (9, 130, 700), 32, (16, 2), 128, "f32"),
     ("f32_d64_gqa4_bs8", 3, (1, 8, 9, 555), 8, (8, 2), 64, "f32"),
+    # kv-head counts that give 2-wave and 1-wave workgroups and several
+    # kv-head groups per grid row (the balanced schedule's slices per group
+    # then differ from 256)
+    ("gqa4_hkv6", 3, (3, 200, 1100, 17), 16, (24, 6), None, None),
+    ("gqa2_hkv5_bs8", 3, (17, 500, 1, 64), 8, (10, 5), None, None),
+    ("mha_hkv3", 2, (33, 900, 2), 16, (3, 3), None, None),
+    ("gqa8_hkv16_bs32", 4, (33, 900, 4097), 32, (128, 16), None, None),
 ]
 
 

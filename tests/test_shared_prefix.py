@@ -134,6 +134,8 @@ CASES = [
     ("gqa8_bs64_long_prefix", 6, 64, (64, 8), [(4160, [1, 2, 3, 4, 5])], [3000]),
     ("prefix_below_a_chunk", 7, 8, (32, 8), [(15, [3, 3]), (16, [0, 1])], [0]),
     ("gqa4_hkv4", 8, 16, (16, 4), [(900, [50] * 5)], [17, 0, 4100]),
+    ("gqa4_hkv6", 9, 16, (24, 6), [(700, [30] * 9), (64, [1, 2])], [5, 1200]),
+    ("gqa2_hkv5_bs8", 10, 8, (10, 5), [(333, [7] * 17)], [0, 900]),
 ]
 
 
@@ -328,7 +330,8 @@ def test_shared_decode_64_prompts_full_size_fp8(ops, full64):
 
 FP8_CASES = [c for c in CASES if c[0] in ("gqa4_bs16", "gqa4_bs8", "gqa4_members_7_9_17",
                                            "gqa2_bs32", "gqa8_bs64_long_prefix",
-                                           "prefix_below_a_chunk", "gqa4_hkv4")]
+                                           "prefix_below_a_chunk", "gqa4_hkv4", "gqa4_hkv6",
+                                           "gqa2_hkv5_bs8")]
 FP8_CASES.append(("mha_hkv8_33_members", 14, 16, (8, 8), [(300, [3] * 33)], [5, 700]))
 
 
